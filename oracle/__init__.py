@@ -1,0 +1,31 @@
+"""Oracle for SDPA-output (G1) gated attention — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, fp64 CPU statement of what the hot path computes, written from
+the pages, used to judge the HIP path.  Only ``tests/``, ``smoke()`` in
+``__graft_entry__.py`` and the ``cpu_baseline`` leg of ``bench.py`` may import it;
+the library and its Python binding never do, and this package imports nothing
+from them.
+
+Sources (page titles; sections):
+  * "GatedAttention [2025]" (huaxiaozhuan.com, a translation of *Gated Attention
+    for Large Language Models: Non-linearity, Sparsity, and Attention-Sink-Free*):
+    §1.2.1 SDPA equation and multi-head concatenation; §1.2.2 gating equation
+    Y' = Y ⊙ σ(X W_θ), granularity (headwise / elementwise), default activation
+    σ(x) = 1/(1+e^{-x}); §1.3.1 GQA explainer; §1.4.1 per-head output equation
+    (causal prefix sum j = 0..i).
+  * "10 · 门控" (llm-infra-atlas): §3.2 position table (G1: after SDPA, per head,
+    before concat) and the GatedAttentionOutput snippet (bias-free projection,
+    view of the gate as [B, T, n_h, d_h] or [B, T, n_h, 1]).
+
+Every function here is pinned by tests in ``tests/test_oracle.py`` (brute-force
+loops, a library SDPA in float64, closed forms and invariants); none is
+"parity unpinned".
+"""
+from .gated_sdpa import (
+    gate_scores, sigmoid, gate_values, sdpa, gated_sdpa, gated_decode,
+    gate_param_count,
+)
+from . import brute
+
+__all__ = ["gate_scores", "sigmoid", "gate_values", "sdpa", "gated_sdpa", "gated_decode",
+           "gate_param_count", "brute"]
