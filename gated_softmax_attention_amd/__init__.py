@@ -1,0 +1,15 @@
+"""gated_softmax_attention_amd — SDPA-output (G1) gated attention for AMD MI355X (gfx950).
+
+Thin Python binding over libgsa.so (see include/gsa.h).  Every step of the
+computation runs in the library's HIP kernels; this module only checks tensor
+properties, allocates outputs with torch and passes device pointers and the
+current HIP stream.  There is no CPU or PyTorch fallback: calls fail loudly
+when the library is missing or no GPU is present.
+"""
+from .ops import (gate_logits, forward, decode, gated_attention, gated_decode,
+                  decode_workspace_bytes, decode_num_splits, MODES)
+from ._lib import GsaError, load as load_library, LIB_PATH
+
+__all__ = ["gate_logits", "forward", "decode", "gated_attention", "gated_decode",
+           "decode_workspace_bytes", "decode_num_splits", "MODES", "GsaError",
+           "load_library", "LIB_PATH"]

@@ -1,0 +1,53 @@
+"""Build libgsa.so (all HIP kernels + the C ABI) in-tree with hipcc for gfx950.
+
+Usage:  python -m gated_softmax_attention_amd.build   (or __graft_entry__.build())
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libgsa.so")
+SOURCES = ["api.hip", "gate_gemm.hip", "attn_fwd.hip", "attn_decode.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    # no packed-fp32 VALU instructions: plain scalar fp32 code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libgsa.so next to this file; return its path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=PKG, prefix=".libgsa.")
+    os.close(fd)
+    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+        if verbose and res.stderr:
+            # hipcc's host pass warns about the gfx-only target feature; keep other lines
+            lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
+            if lines:
+                print("\n".join(lines[-40:]), file=sys.stderr)
+        shutil.move(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

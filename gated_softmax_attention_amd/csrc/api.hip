@@ -1,0 +1,219 @@
+// libgsa C ABI: argument validation, device checks, dispatch to the gfx950 kernels.
+// The declarations and their contracts are in include/gsa.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "gsa.h"
+
+namespace gsa {
+hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, int64_t K, int64_t N,
+                            bool bf16_inputs, bool apply_sigmoid, hipStream_t stream);
+hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                           int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
+                           bool bf16_inputs, hipStream_t stream);
+hipError_t launch_decode_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                              void* workspace, int B, int L, int Hq, int Hkv, int D, int mode,
+                              int nsplit, hipStream_t stream);
+int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv);
+int64_t decode_chunk(int64_t L, int64_t nsplit);
+}  // namespace gsa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gsa_status fail(gsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gsa_status ok() {
+  g_last_error.clear();
+  return GSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kIntMax = 0x7fffffff;
+
+// Per-device check that the device is a gfx950 part, done once per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = other
+char g_dev_arch[kMaxDevices][64];
+
+gsa_status check_device() {
+  int dev = -1;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(GSA_ERR_NO_DEVICE, "no HIP device is visible");
+  }
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(GSA_ERR_NO_DEVICE, "hipGetDevice failed");
+  }
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      snprintf(g_dev_arch[dev], sizeof g_dev_arch[dev], "%s", prop.gcnArchName);
+      g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    } else {
+      (void)hipGetLastError();
+      snprintf(g_dev_arch[dev], sizeof g_dev_arch[dev], "unknown");
+      g_dev_ok[dev] = 0;
+    }
+  });
+  if (!g_dev_ok[dev])
+    return fail(GSA_ERR_UNSUPPORTED, "device %d is %s; libgsa is built for gfx950 only", dev,
+                g_dev_arch[dev]);
+  return GSA_OK;
+}
+
+gsa_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+gsa_status check_dtype(const char* fn, int dtype) {
+  if (dtype != GSA_FP32 && dtype != GSA_BF16)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: dtype %d is not GSA_FP32 or GSA_BF16", fn, dtype);
+  return GSA_OK;
+}
+
+gsa_status check_attn_shape(const char* fn, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                            int mode, const float* G) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0)
+    return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%lld S=%lld Hq=%lld Hkv=%lld D=%lld)",
+                fn, (long long)B, (long long)S, (long long)Hq, (long long)Hkv, (long long)D);
+  if (Hq % Hkv != 0)
+    return fail(GSA_ERR_INVALID_ARG, "%s: Hq=%lld is not a multiple of Hkv=%lld", fn, (long long)Hq,
+                (long long)Hkv);
+  if (mode != GSA_GATE_NONE && mode != GSA_GATE_ELEMENTWISE && mode != GSA_GATE_HEADWISE)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown gate mode %d", fn, mode);
+  if ((mode == GSA_GATE_NONE) != (G == nullptr))
+    return fail(GSA_ERR_INVALID_ARG, "%s: G must be NULL exactly when mode is GSA_GATE_NONE", fn);
+  if (D != 64 && D != 128)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: head dim %lld is not supported (64 or 128)", fn, (long long)D);
+  if (B * S > kIntMax || Hq > 4096 || Hkv > 4096 || S > kIntMax)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gsa_version(void) { return 100; }
+
+const char* gsa_status_string(int status) {
+  switch (status) {
+    case GSA_OK: return "GSA_OK";
+    case GSA_ERR_INVALID_ARG: return "GSA_ERR_INVALID_ARG";
+    case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED";
+    case GSA_ERR_MISALIGNED: return "GSA_ERR_MISALIGNED";
+    case GSA_ERR_WORKSPACE: return "GSA_ERR_WORKSPACE";
+    case GSA_ERR_NO_DEVICE: return "GSA_ERR_NO_DEVICE";
+    case GSA_ERR_HIP: return "GSA_ERR_HIP";
+    default: return "GSA_ERR_UNKNOWN";
+  }
+}
+
+const char* gsa_last_error_message(void) { return g_last_error.c_str(); }
+
+gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, int64_t d_model,
+                           int64_t N, int dtype, int apply_sigmoid, void* stream) {
+  if (!X || !W || !G) return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: null pointer");
+  if (M <= 0 || d_model <= 0 || N <= 0)
+    return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: sizes must be positive (M=%lld d_model=%lld N=%lld)",
+                (long long)M, (long long)d_model, (long long)N);
+  if (gsa_status st = check_dtype("gsa_gate_logits", dtype)) return st;
+  if (apply_sigmoid != 0 && apply_sigmoid != 1)
+    return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: apply_sigmoid must be 0 or 1");
+  if (d_model % 8 != 0)
+    return fail(GSA_ERR_UNSUPPORTED, "gsa_gate_logits: d_model=%lld is not a multiple of 8",
+                (long long)d_model);
+  if (M > kIntMax || d_model > kIntMax || N > kIntMax)
+    return fail(GSA_ERR_UNSUPPORTED, "gsa_gate_logits: sizes exceed the supported range");
+  if (!aligned16(X) || !aligned16(W) || !aligned16(G))
+    return fail(GSA_ERR_MISALIGNED, "gsa_gate_logits: X, W and G must be 16-byte aligned");
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_gate_gemm(X, W, G, M, d_model, N, dtype == GSA_BF16, apply_sigmoid == 1,
+                                          (hipStream_t)stream),
+                    "gsa_gate_logits launch");
+}
+
+gsa_status gsa_forward(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                       int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype,
+                       void* stream) {
+  if (!Q || !K || !V || !Y) return fail(GSA_ERR_INVALID_ARG, "gsa_forward: null pointer");
+  if (gsa_status st = check_attn_shape("gsa_forward", B, S, Hq, Hkv, D, mode, G)) return st;
+  if (gsa_status st = check_dtype("gsa_forward", dtype)) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "gsa_forward: Q, K, V, G and Y must be 16-byte aligned");
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_attn_fwd(Q, K, V, G, Y, (int)B, (int)S, (int)S, (int)Hq, (int)Hkv, (int)D,
+                                         mode, dtype == GSA_BF16, (hipStream_t)stream),
+                    "gsa_forward launch");
+}
+
+int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int num_splits) {
+  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || num_splits < 0) return 0;
+  int64_t ns = num_splits > 0 ? num_splits : gsa::decode_auto_splits(B, L, Hq, Hkv);
+  if (ns > L) ns = L;
+  // every split gets at least one key: the effective count after rounding the chunk
+  const int64_t chunk = gsa::decode_chunk(L, ns);
+  return (L + chunk - 1) / chunk;
+}
+
+size_t gsa_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int num_splits) {
+  const int64_t ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+  if (ns == 0) return 0;
+  return (size_t)(B * Hq * ns * (D + 4)) * sizeof(float);
+}
+
+gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
+                      int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !Kc || !Vc || !Y) return fail(GSA_ERR_INVALID_ARG, "gsa_decode: null pointer");
+  if (gsa_status st = check_attn_shape("gsa_decode", B, L, Hq, Hkv, D, mode, G)) return st;
+  if (gsa_status st = check_dtype("gsa_decode", dtype)) return st;
+  if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "gsa_decode: num_splits must be >= 0");
+  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "gsa_decode: B*L exceeds the supported range");
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "gsa_decode: Q, Kc, Vc, G and Y must be 16-byte aligned");
+  size_t need = 0;
+  int64_t ns = 0;
+  if (dtype == GSA_BF16) {
+    ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+    need = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(GSA_ERR_WORKSPACE, "gsa_decode: workspace of %zu bytes needed, %zu given", need,
+                  workspace_bytes);
+    if (workspace && !aligned16(workspace))
+      return fail(GSA_ERR_MISALIGNED, "gsa_decode: workspace must be 16-byte aligned");
+  }
+  if (gsa_status st = check_device()) return st;
+  if (dtype == GSA_BF16)
+    return hip_result(gsa::launch_decode_bf16(Q, Kc, Vc, G, Y, workspace, (int)B, (int)L, (int)Hq,
+                                              (int)Hkv, (int)D, mode, (int)ns, (hipStream_t)stream),
+                      "gsa_decode launch");
+  // float32: the general kernel with one query row aligned to the end of the cache
+  return hip_result(gsa::launch_attn_fwd(Q, Kc, Vc, G, Y, (int)B, 1, (int)L, (int)Hq, (int)Hkv, (int)D,
+                                         mode, false, (hipStream_t)stream),
+                    "gsa_decode launch");
+}
+
+}  // extern "C"

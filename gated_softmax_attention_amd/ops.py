@@ -1,0 +1,118 @@
+"""torch-facing wrappers with the C ABI's names: argument marshalling only."""
+import torch
+
+from . import _lib
+
+MODES = {"none": _lib.GSA_GATE_NONE, "elementwise": _lib.GSA_GATE_ELEMENTWISE,
+         "headwise": _lib.GSA_GATE_HEADWISE}
+_DTYPES = {torch.float32: _lib.GSA_FP32, torch.bfloat16: _lib.GSA_BF16}
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(*ts):
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+    for t in ts[1:]:
+        if t.dtype != dt:
+            raise TypeError("X/W or Q/K/V/Y tensors must share one dtype")
+    return _DTYPES[dt]
+
+
+def gate_logits(X, W, G=None, apply_sigmoid=True, stream=None):
+    """G = σ(X·W_θ) (or the logits Z when apply_sigmoid is False), float32 [M, N].
+
+    X: [..., d_model] (leading dims flattened to M rows); W: [d_model, N].
+    """
+    dm = X.shape[-1]
+    M = X.numel() // dm
+    N = W.shape[1]
+    if W.shape[0] != dm:
+        raise ValueError(f"W has {W.shape[0]} rows, X has d_model={dm}")
+    if G is None:
+        G = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif G.dtype != torch.float32 or G.numel() != M * N:
+        raise ValueError("G must be float32 with M*N elements")
+    lib = _lib.load()
+    _lib.check(lib.gsa_gate_logits(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N,
+                                   _dtype(X, W), int(bool(apply_sigmoid)), _stream(stream)))
+    return G
+
+
+def _mode(mode):
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {list(MODES)}")
+    return MODES[mode]
+
+
+def forward(Q, K, V, G, mode, Y=None, stream=None):
+    """Causal gated SDPA, Y' [B, S, Hq, D] from Q [B,S,Hq,D], K/V [B,S,Hkv,D] and G."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    gp = None if G is None else _dev(G, "G")
+    lib = _lib.load()
+    _lib.check(lib.gsa_forward(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), gp, _dev(Y, "Y"),
+                               B, S, Hq, Hkv, D, _mode(mode), _dtype(Q, K, V, Y), _stream(stream)))
+    return Y
+
+
+def decode_num_splits(B, L, Hq, Hkv, D, num_splits=0):
+    return int(_lib.load().gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits))
+
+
+def decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits=0):
+    return int(_lib.load().gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits))
+
+
+def decode(Q, Kc, Vc, G, mode, num_splits=0, Y=None, workspace=None, stream=None):
+    """One decode step: Q [B,1,Hq,D] against the cache Kc/Vc [B,L,Hkv,D]."""
+    B, one, Hq, D = Q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per batch")
+    L, Hkv = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    need = decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    gp = None if G is None else _dev(G, "G")
+    lib = _lib.load()
+    _lib.check(lib.gsa_decode(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), gp, _dev(Y, "Y"),
+                              B, L, Hq, Hkv, D, _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits,
+                              wp, wbytes, _stream(stream)))
+    return Y
+
+
+def gated_attention(X, W, Q, K, V, mode, stream=None):
+    """The whole prefill path: gate projection + sigmoid, then causal gated SDPA."""
+    G = None if mode == "none" else gate_logits(X, W, stream=stream)
+    return forward(Q, K, V, G, mode, stream=stream)
+
+
+def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, stream=None):
+    """The whole decode path: gate projection + sigmoid for the new token, then decode."""
+    G = None if mode == "none" else gate_logits(X, W, stream=stream)
+    return decode(Q, Kc, Vc, G, mode, num_splits=num_splits, stream=stream)

@@ -1,0 +1,133 @@
+/*
+ * gsa.h — C ABI of libgsa: SDPA-output ("G1") gated attention on AMD MI355X (gfx950).
+ *
+ * The operation, as the "GatedAttention [2025]" page states it:
+ *   Y  = softmax(Q·Kᵀ / √d_k + causal mask) · V            (§1.2.1 SDPA equation,
+ *                                                            causal per §1.4.1 eq.)
+ *   Y' = Y ⊙ σ(X·W_θ),  σ(x) = 1 / (1 + e^{-x})            (§1.2.2 gating equation and
+ *                                                            default activation)
+ * applied per query head before the heads are concatenated (G1 position:
+ * "10 · 门控" page, §3.2 position table).  The gate is elementwise (one score per
+ * head and head dimension, shape n×q×d_k) or headwise (one scalar per head and
+ * token, shape n×q) ("GatedAttention [2025]" §1.2.2, granularity (2)).  Key/value
+ * heads are shared by groups of query heads (GQA, "GatedAttention [2025]" §1.3.1):
+ * query head h reads key/value head h / (Hq / Hkv).
+ *
+ * Conventions for every entry point:
+ *  - Pointers X, W, G, Q, K, V, Y, workspace are DEVICE pointers owned by the
+ *    caller, to contiguous row-major tensors, each 16-byte aligned.  The library
+ *    allocates nothing and keeps no per-call state.
+ *  - dtype (gsa_dtype) is the element type of X, W, Q, K, V and Y'.  G is always
+ *    float32.  Arithmetic is float32 (bf16 inputs multiply exactly into float32
+ *    accumulators on the matrix cores).
+ *  - Calls only ENQUEUE work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return; results are visible after the caller synchronises.
+ *  - Errors are returned as gsa_status; nothing aborts and no exception crosses
+ *    the ABI.  All argument checks run before any HIP call, so they also work on
+ *    a host without a GPU (which then gets GSA_ERR_NO_DEVICE).  A per-thread
+ *    message describing the last failure is available from
+ *    gsa_last_error_message().
+ *  - Calls are thread-safe; concurrent calls on different streams are allowed.
+ */
+#ifndef GSA_H
+#define GSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gsa_status {
+  GSA_OK = 0,
+  GSA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, Hq % Hkv != 0, mode/G mismatch */
+  GSA_ERR_UNSUPPORTED = 2,   /* a head dim, dtype, mode or device the library does not handle */
+  GSA_ERR_MISALIGNED = 3,    /* a pointer not 16-byte aligned */
+  GSA_ERR_WORKSPACE = 4,     /* decode workspace missing or smaller than required */
+  GSA_ERR_NO_DEVICE = 5,     /* no HIP device visible to the calling thread */
+  GSA_ERR_HIP = 6            /* a HIP runtime or kernel-launch error */
+} gsa_status;
+
+typedef enum gsa_dtype { GSA_FP32 = 0, GSA_BF16 = 1 } gsa_dtype;
+
+typedef enum gsa_gate_mode {
+  GSA_GATE_NONE = 0,         /* plain causal SDPA, no gate (G must be NULL) */
+  GSA_GATE_ELEMENTWISE = 1,  /* G is [rows, Hq*D]; column h*D + d gates head h, dim d */
+  GSA_GATE_HEADWISE = 2      /* G is [rows, Hq];   column h gates all of head h       */
+} gsa_gate_mode;
+
+/* Library version, encoded as major*10000 + minor*100 + patch. */
+int gsa_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* gsa_status_string(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* gsa_last_error_message(void);
+
+/*
+ * Gate projection with fused sigmoid: G = σ(X·W_θ) ("GatedAttention [2025]"
+ * §1.2.2 gating equation; no bias, as the §3.2 snippet on "10 · 门控" has
+ * bias=False).
+ *   X : [M, d_model] of dtype   (M = B*S token rows, the hidden states after pre-norm)
+ *   W : [d_model, N] of dtype   (N = Hq*D elementwise, Hq headwise)
+ *   G : [M, N] float32 output
+ *   apply_sigmoid: 1 stores σ(Z), 0 stores the raw logits Z = X·W_θ.
+ * Requires d_model % 8 == 0.  Sizes must be positive.
+ */
+gsa_status gsa_gate_logits(const void* X, const void* W, float* G,
+                           int64_t M, int64_t d_model, int64_t N,
+                           int dtype, int apply_sigmoid, void* stream);
+
+/*
+ * Causal gated SDPA forward (prefill): for every batch b, query head h and
+ * query row i,  Y'[b,i,h,:] = (Σ_{j<=i} P_ij V[b,j,h/(Hq/Hkv),:]) ⊙ gate,
+ * P_i = softmax_j(Q[b,i,h,:]·K[b,j,c,:] / √D) over j <= i (self included).
+ *   Q : [B, S, Hq, D]   K, V : [B, S, Hkv, D]   (dtype)
+ *   G : [B*S, Hq*D] (ELEMENTWISE) or [B*S, Hq] (HEADWISE) float32 scores from
+ *       gsa_gate_logits; must be NULL iff mode == GSA_GATE_NONE
+ *   Y : [B, S, Hq, D] output (dtype); the ungated SDPA output is never stored.
+ * Requires D in {64, 128} and Hq % Hkv == 0.
+ */
+gsa_status gsa_forward(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                       int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                       int mode, int dtype, void* stream);
+
+/*
+ * Split count gsa_decode will use for these sizes: num_splits itself if > 0,
+ * otherwise the automatic choice.  Returns 0 for invalid sizes.
+ */
+int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                              int num_splits);
+
+/* Workspace bytes gsa_decode needs for these sizes (0 for invalid sizes). */
+size_t gsa_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int num_splits);
+
+/*
+ * One decode step: a single query token per batch against a contiguous KV
+ * cache of length L that already holds that token, so the query attends to
+ * all L keys (the KV cache of the "GatedAttention [2025]" §1.3.1 GQA
+ * explainer).  Same definition as gsa_forward with one query row per batch
+ * sitting at position L-1.
+ *   Q  : [B, 1, Hq, D]    Kc, Vc : [B, L, Hkv, D]   (dtype)
+ *   G  : [B, Hq*D] or [B, Hq] float32 (see gsa_forward), NULL iff mode NONE
+ *   Y  : [B, 1, Hq, D] output (dtype)
+ *   num_splits: 0 = automatic; otherwise the number of chunks the cache is cut
+ *     into along L (each chunk's partial max, sum and weighted values are
+ *     merged exactly at the end).
+ *   workspace: device scratch of at least gsa_decode_workspace_bytes(...) bytes
+ *     (may be NULL when that is 0).  Its contents on entry do not matter.
+ * Requires D in {64, 128} and Hq % Hkv == 0.
+ */
+gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y,
+                      int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                      int mode, int dtype, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* GSA_H */

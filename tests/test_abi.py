@@ -1,0 +1,136 @@
+"""The C ABI of libgsa on the host: every declared symbol is exported, and the
+argument checks return the documented status codes before any HIP call.
+
+These tests never hand the library a pointer that a kernel could dereference:
+every call either fails validation, or (only on a host without a GPU) stops at
+the device check with GSA_ERR_NO_DEVICE.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_softmax_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsa.h")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
+MIS = FAKE + 4   # misaligned
+
+
+def have_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_softmax_attention_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gsa_version() == 100
+    for code, name in [(0, b"GSA_OK"), (1, b"GSA_ERR_INVALID_ARG"), (2, b"GSA_ERR_UNSUPPORTED"),
+                       (3, b"GSA_ERR_MISALIGNED"), (4, b"GSA_ERR_WORKSPACE"),
+                       (5, b"GSA_ERR_NO_DEVICE"), (6, b"GSA_ERR_HIP"), (99, b"GSA_ERR_UNKNOWN")]:
+        assert lib.gsa_status_string(code) == name
+
+
+def fwd(lib, Q=FAKE, K=FAKE, V=FAKE, G=FAKE, Y=FAKE, B=1, S=8, Hq=4, Hkv=2, D=128, mode=1, dtype=1):
+    return lib.gsa_forward(Q, K, V, G, Y, B, S, Hq, Hkv, D, mode, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(Y=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(B=0), _lib.GSA_ERR_INVALID_ARG),
+    (dict(S=-3), _lib.GSA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.GSA_ERR_INVALID_ARG),
+    (dict(mode=7), _lib.GSA_ERR_INVALID_ARG),
+    (dict(mode=0), _lib.GSA_ERR_INVALID_ARG),       # G given with mode NONE
+    (dict(G=None, mode=1), _lib.GSA_ERR_INVALID_ARG),
+    (dict(G=None, mode=2), _lib.GSA_ERR_INVALID_ARG),
+    (dict(D=96), _lib.GSA_ERR_UNSUPPORTED),
+    (dict(D=256), _lib.GSA_ERR_UNSUPPORTED),
+    (dict(dtype=5), _lib.GSA_ERR_UNSUPPORTED),
+    (dict(K=MIS), _lib.GSA_ERR_MISALIGNED),
+    (dict(G=MIS), _lib.GSA_ERR_MISALIGNED),
+])
+def test_forward_argument_checks(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.gsa_last_error_message().decode().startswith("gsa_forward")
+
+
+def test_gate_logits_argument_checks(lib):
+    gl = lambda X=FAKE, W=FAKE, G=FAKE, M=4, dm=64, N=8, dt=1, sig=1: lib.gsa_gate_logits(
+        X, W, G, M, dm, N, dt, sig, None)
+    assert gl(X=None) == _lib.GSA_ERR_INVALID_ARG
+    assert gl(M=0) == _lib.GSA_ERR_INVALID_ARG
+    assert gl(N=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert gl(sig=2) == _lib.GSA_ERR_INVALID_ARG
+    assert gl(dt=3) == _lib.GSA_ERR_UNSUPPORTED
+    assert gl(dm=60) == _lib.GSA_ERR_UNSUPPORTED
+    assert gl(W=MIS) == _lib.GSA_ERR_MISALIGNED
+
+
+def test_decode_argument_checks(lib):
+    def dec(Q=FAKE, G=FAKE, B=2, L=100, Hq=8, Hkv=2, D=128, mode=1, dtype=1, ns=0, ws=FAKE, wsb=1 << 30):
+        return lib.gsa_decode(Q, FAKE, FAKE, G, FAKE, B, L, Hq, Hkv, D, mode, dtype, ns, ws, wsb, None)
+    assert dec(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(L=0) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(ns=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(G=None) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(D=32) == _lib.GSA_ERR_UNSUPPORTED
+    assert dec(wsb=16) == _lib.GSA_ERR_WORKSPACE
+    assert dec(ws=None) == _lib.GSA_ERR_WORKSPACE
+    assert dec(ws=MIS) == _lib.GSA_ERR_MISALIGNED
+
+
+def test_decode_split_arithmetic(lib):
+    # requested counts are honoured up to the chunk rounding; every split is non-empty
+    for L, ns in [(16384, 16), (1, 0), (1, 4), (63, 0), (1025, 3), (100, 7), (16384, 0)]:
+        eff = lib.gsa_decode_num_splits(64, L, 32, 8, 128, ns)
+        assert 1 <= eff <= max(ns, eff)
+        chunk = -(-L // eff)
+        chunk = -(-chunk // 16) * 16
+        assert (eff - 1) * chunk < L <= eff * chunk or eff == 1
+        assert lib.gsa_decode_workspace_bytes(64, L, 32, 8, 128, ns) == 64 * 32 * eff * (128 + 4) * 4
+    assert lib.gsa_decode_num_splits(0, 10, 4, 4, 128, 0) == 0
+    assert lib.gsa_decode_workspace_bytes(2, 10, 4, 3, 128, 0) == 0
+
+
+@pytest.mark.skipif("have_gpu()", reason="a GPU is visible: valid-looking fake pointers must not be launched")
+def test_valid_arguments_without_a_gpu_report_no_device(lib):
+    assert fwd(lib) == _lib.GSA_ERR_NO_DEVICE
+    assert lib.gsa_gate_logits(FAKE, FAKE, FAKE, 4, 64, 8, 1, 1, None) == _lib.GSA_ERR_NO_DEVICE
+    assert "device" in lib.gsa_last_error_message().decode()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import gated_softmax_attention_amd as gsa
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gsa.gate_logits(x, w, G=torch.zeros(4, 8))

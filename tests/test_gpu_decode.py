@@ -1,0 +1,96 @@
+"""Split-K gated decode on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_softmax_attention_amd as gsa
+from synth import CONFIGS, make_inputs
+from helpers import TOL, f64, report, guarded_empty, guard_ok
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dec_cfg(B, L, Hq, Hkv, D, mode, dtype, dm=64):
+    return CONFIGS["decode"].with_(name="d", B=B, L=L, Hq=Hq, Hkv=Hkv, D=D, mode=mode, dtype=dtype,
+                                   d_model=dm)
+
+
+def run(inp, mode, num_splits=0):
+    Q = inp["Q"]
+    G = None if mode == "none" else gsa.gate_logits(inp["X"], inp["W"])
+    Y, g = guarded_empty(tuple(Q.shape), Q.dtype, DEV)
+    gsa.decode(Q, inp["K"], inp["V"], G, mode, num_splits=num_splits, Y=Y)
+    torch.cuda.synchronize()
+    assert guard_ok(g)
+    return Y, G
+
+
+def oracle_decode(inp, mode, batches=None):
+    bs = slice(None) if batches is None else batches
+    return oracle.gated_decode(f64(inp["X"][bs]), f64(inp["W"]), f64(inp["Q"][bs]), f64(inp["K"][bs]),
+                               f64(inp["V"][bs]), mode)
+
+
+CASES = []
+for (B, L, Hq, Hkv) in [(1, 1, 4, 1), (2, 15, 4, 4), (3, 16, 8, 2), (2, 63, 8, 1), (1, 1025, 32, 8),
+                        (2, 3000, 16, 2), (4, 777, 12, 2), (1, 4096, 4, 4)]:
+    for D in (128, 64):
+        for mode in ("elementwise", "headwise"):
+            CASES.append((B, L, Hq, Hkv, D, mode))
+CASES.append((2, 500, 8, 2, 128, "none"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,L,Hq,Hkv,D,mode", CASES)
+def test_small_decode(B, L, Hq, Hkv, D, mode, dtype):
+    inp = make_inputs(dec_cfg(B, L, Hq, Hkv, D, mode, dtype), seed=L + Hq, device=DEV)
+    Y, _ = run(inp, mode)
+    report(f64(Y), oracle_decode(inp, mode), TOL[dtype], f"{dtype} B{B} L{L} {Hq}/{Hkv} D{D} {mode}")
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 7, 16, 64])
+def test_split_counts_agree(ns):
+    inp = make_inputs(dec_cfg(2, 2049, 8, 2, 128, "elementwise", "bf16"), seed=9, device=DEV)
+    want = oracle_decode(inp, "elementwise")
+    Y, _ = run(inp, "elementwise", num_splits=ns)
+    report(f64(Y), want, TOL["bf16"], f"splits {ns} (effective "
+           f"{gsa.decode_num_splits(2, 2049, 8, 2, 128, ns)})")
+
+
+def test_decode_matches_last_prefill_row():
+    """Decode of token L-1 against the cache equals row L-1 of the prefill forward."""
+    L = 700
+    cfg = CONFIGS["tiny_fp32"].with_(name="p", B=2, S=L, Hq=8, Hkv=2, D=128, d_model=64,
+                                     mode="elementwise", dtype="bf16")
+    inp = make_inputs(cfg, seed=5, device=DEV)
+    G = gsa.gate_logits(inp["X"], inp["W"])
+    Yp = gsa.forward(inp["Q"], inp["K"], inp["V"], G, "elementwise")
+    dec = {"X": inp["X"][:, -1:].contiguous(), "W": inp["W"], "Q": inp["Q"][:, -1:].contiguous(),
+           "K": inp["K"], "V": inp["V"]}
+    Yd, _ = run(dec, "elementwise")
+    report(f64(Yd), f64(Yp[:, -1:]), TOL["bf16"], "decode vs prefill last row")
+    report(f64(Yd), oracle_decode(dec, "elementwise"), TOL["bf16"], "decode vs oracle")
+
+
+def test_saturated_gate_decode_equals_ungated_bitwise():
+    inp = make_inputs(dec_cfg(2, 1000, 8, 2, 128, "elementwise", "bf16"), seed=2, device=DEV)
+    inp["W"].zero_()
+    inp["W"][0, :] = 1.0
+    inp["X"][..., 0] = 40.0
+    Yg, G = run(inp, "elementwise")
+    assert bool((G == 1.0).all())
+    Yn, _ = run(inp, "none")
+    assert torch.equal(Yg.view(torch.int16), Yn.view(torch.int16))
+
+
+def test_full_size_decode_config():
+    cfg = CONFIGS["decode"]
+    print("  decode: generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    Y, _ = run(inp, cfg.mode)
+    assert not torch.isnan(Y.float()).any()
+    bs = [0, 17, 63]
+    want = oracle_decode(inp, cfg.mode, batches=bs)
+    report(f64(Y[bs]), want, TOL["bf16"], f"decode full size, batches {bs}")
