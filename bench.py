@@ -1,0 +1,270 @@
+"""Benchmark of the gated SDPA hot path on one MI355X.
+
+One step = the whole prefill path on the bf16 dense-prefill workload (batch 2,
+seq 4096, d_model 2048, 16 query / 16 key-value heads, head dim 128,
+elementwise gate): gsa_gate_logits (σ(X·W_θ)) then gsa_forward (causal gated
+SDPA).  Inputs are seeded synthetic tensors already resident in HBM.
+
+Reported (one JSON line): whole-step TFLOP/s; the roofline of the dominant
+kernel (the gated forward), timed per launch with HIP events on the stream it
+runs on; the decode workload (batch 64, one token against a 16384-long KV
+cache, 32/8 heads) as GB/s with its own roofline; and the fp64 oracle timed on
+the host cores on a bounded sample of the prefill workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gated_softmax_attention_amd", "csrc")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+                   help="run one workload's GPU part only (for profiling)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run only a plain device copy of this many MiB (HBM counter calibration)")
+    return p.parse_args()
+
+
+def src_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, sources):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != src_hash(*sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_steps(step, kernel, steps, warmup, torch):
+    """Run warmup + timed steps; events bracket the whole region and each launch
+    of the dominant kernel, all recorded on the current stream."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    k_start = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    k_end = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(st)
+    for i in range(steps):
+        step((k_start[i], k_end[i], st))
+    t_end.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    k_ms = sum(k_start[i].elapsed_time(k_end[i]) for i in range(steps)) / steps
+    return total_ms / steps, k_ms, wall
+
+
+def prefill_bench(args, torch, gsa, cfg):
+    from synth import make_inputs
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    G = torch.empty((cfg.B * cfg.S, cfg.N), dtype=torch.float32, device="cuda:0")
+    Y = torch.empty_like(Q)
+
+    def step(ev):
+        gsa.gate_logits(X, W, G=G)
+        if ev:
+            ev[0].record(ev[2])
+        gsa.forward(Q, K, V, G, cfg.mode, Y=Y)
+        if ev:
+            ev[1].record(ev[2])
+
+    ms, fwd_ms, wall = time_steps(step, "attn", args.steps, args.warmup, torch)
+    if torch.isnan(Y[:, :64].float()).any():
+        raise RuntimeError("NaN in output")
+    flops = cfg.total_flops()
+    fwd_flops = cfg.attention_flops()
+    achieved = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    traffic = measured_traffic("attn_fwd_dense_prefill", ["attn_fwd.hip", "common.h"])
+    return {
+        "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "wall_s": wall,
+        "roofline": {
+            "kernel": "attn_fwd_bf16_kernel<128, elementwise>",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "avg_launch_ms": fwd_ms, "algorithmic_flops_per_launch": fwd_flops,
+        },
+        "gate_ms_per_step": ms - fwd_ms,
+    }
+
+
+def decode_bench(args, torch, gsa, cfg):
+    from synth import make_inputs
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    G = torch.empty((cfg.B, cfg.N), dtype=torch.float32, device="cuda:0")
+    Y = torch.empty_like(Q)
+    ns = gsa.decode_num_splits(cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.D)
+    ws = torch.empty(gsa.decode_workspace_bytes(cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.D),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def step(ev):
+        gsa.gate_logits(X, W, G=G)
+        if ev:
+            ev[0].record(ev[2])
+        gsa.decode(Q, K, V, G, cfg.mode, Y=Y, workspace=ws)
+        if ev:
+            ev[1].record(ev[2])
+
+    ms, dec_ms, wall = time_steps(step, "decode", args.steps, args.warmup, torch)
+    if torch.isnan(Y.float()).any():
+        raise RuntimeError("NaN in decode output")
+    nbytes = cfg.decode_bytes()
+    kv = nbytes["kv"] + nbytes["q"] + nbytes["y"]   # what the decode call itself must move
+    achieved = kv / (dec_ms * 1e-3) / 1e9
+    traffic = measured_traffic("decode_split", ["attn_decode.hip", "common.h"])
+    return {
+        "workload": "decode", "metric": "decode GB/s (% of HBM peak)",
+        "value": nbytes["total"] / (ms * 1e-3) / 1e9, "unit": "GB/s",
+        "ms_per_step": ms, "pct_of_peak": 100.0 * nbytes["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "config": {"B": cfg.B, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "d_model": cfg.d_model, "mode": cfg.mode, "num_splits": ns},
+        "roofline": {
+            "kernel": "gsa_decode (split + merge)", "bound": "hbm", "achieved": achieved,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic, "avg_launch_ms": dec_ms, "algorithmic_bytes_per_launch": kv,
+        },
+    }
+
+
+def cpu_baseline(args, torch, cfg):
+    """The fp64 oracle, as it is, on a bounded sample of the prefill workload:
+    every query row r with r % stride == 0 (all batches and heads), with the
+    smallest power-of-two stride whose estimated time fits --cpu-seconds
+    (stride 1 = the whole workload)."""
+    import numpy as np
+    import oracle
+    from synth import make_inputs, to_float64_numpy as f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    a = {k: f64(inp[k]) for k in "XWQKV"}
+    del inp
+
+    def run(stride):
+        rows = np.arange(0, cfg.S, stride)
+        t0 = time.perf_counter()
+        oracle.gated_sdpa(a["X"], a["W"], a["Q"], a["K"], a["V"], cfg.mode, rows=rows)
+        dt = time.perf_counter() - t0
+        pairs = int((rows + 1).sum())
+        flops = 4 * cfg.D * cfg.B * cfg.Hq * pairs + 2 * cfg.B * len(rows) * cfg.d_model * cfg.N
+        return dt, flops, len(rows)
+
+    dt, fl, n = run(64)                       # calibration on 1/64 of the rows
+    stride = 1
+    while stride < 64 and dt * (64 / stride) > args.cpu_seconds:
+        stride *= 2
+    dt, fl, n = run(stride)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"dense_prefill workload, query rows i % {stride} == 0 ({n} of {cfg.S} rows, "
+                      f"all {cfg.B} batches x {cfg.Hq} heads): {fl:.3e} algorithmic flops (gate + "
+                      f"causal attention) in fp64 numpy"}
+
+
+def copy_calibration(mib, torch):
+    n = mib * (1 << 20)
+    x = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, torch)
+        return
+    import gated_softmax_attention_amd as gsa
+    from synth import CONFIGS
+    gsa.load_library()
+    torch.cuda.set_device(0)
+
+    pcfg = CONFIGS["dense_prefill"]
+    dcfg = CONFIGS["decode"]
+    out = None
+    if args.only != "decode":
+        pre = prefill_bench(args, torch, gsa, pcfg)
+        print(f"# prefill: {pre['ms_per_step']:.4f} ms/step, {pre['tflops']:.1f} TFLOP/s; forward "
+              f"{pre['roofline']['avg_launch_ms']:.4f} ms = {pre['roofline']['achieved']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        out = {
+            "metric": "gated causal SDPA fwd TFLOP/s (gate GEMM + gated forward, % of bf16 MFMA peak)",
+            "value": pre["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": pre["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "pct_of_peak": 100.0 * pre["tflops"] / PEAK_BF16_TFLOPS,
+            "config": {"workload": "dense_prefill", "B": pcfg.B, "S": pcfg.S, "d_model": pcfg.d_model,
+                       "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "D": pcfg.D, "mode": pcfg.mode,
+                       "causal": True, "flops_per_step": pcfg.total_flops()},
+            "roofline": pre["roofline"],
+            "gate_ms_per_step": pre["gate_ms_per_step"],
+        }
+    if not args.no_decode and args.only != "prefill":
+        dec = decode_bench(args, torch, gsa, dcfg)
+        print(f"# decode: {dec['ms_per_step']:.4f} ms/step, {dec['value']:.1f} GB/s; decode call "
+              f"{dec['roofline']['avg_launch_ms']:.4f} ms = {dec['roofline']['achieved']:.1f} GB/s",
+              file=sys.stderr, flush=True)
+        if out is None:
+            out = {"metric": dec["metric"], "value": dec["value"], "unit": "GB/s", "n_gpus": 1,
+                   "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+                   "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                   "dtype": "bf16", "data": "synthetic", "config": {"workload": "decode"},
+                   "roofline": dec["roofline"]}
+        else:
+            out["decode"] = dec
+    if out is not None and not args.no_cpu_baseline and args.only is None:
+        print("# timing the oracle on the host ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args, torch, pcfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
