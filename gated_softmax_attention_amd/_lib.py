@@ -2,7 +2,8 @@
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
+# GSA_LIBRARY_PATH selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("GSA_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
 
 GSA_OK = 0
 GSA_ERR_INVALID_ARG = 1

@@ -25,12 +25,12 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libgsa.so next to this file; return its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def build(verbose: bool = False, out: str = LIB_PATH, csrc: str = CSRC, extra=()) -> str:
+    """Compile every source into libgsa.so (next to this file by default); return its path."""
+    srcs = [os.path.join(csrc, s) for s in SOURCES]
     fd, tmp = tempfile.mkstemp(suffix=".so", dir=PKG, prefix=".libgsa.")
     os.close(fd)
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    cmd = [HIPCC, "-I", csrc] + FLAGS + list(extra) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     try:
@@ -42,11 +42,11 @@ def build(verbose: bool = False) -> str:
             lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
             if lines:
                 print("\n".join(lines[-40:]), file=sys.stderr)
-        shutil.move(tmp, LIB_PATH)
+        shutil.move(tmp, out)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
-    return LIB_PATH
+    return out
 
 
 if __name__ == "__main__":

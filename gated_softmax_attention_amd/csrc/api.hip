@@ -108,6 +108,9 @@ gsa_status check_attn_shape(const char* fn, int64_t B, int64_t S, int64_t Hq, in
     return fail(GSA_ERR_UNSUPPORTED, "%s: head dim %lld is not supported (64 or 128)", fn, (long long)D);
   if (B * S > kIntMax || Hq > 4096 || Hkv > 4096 || S > kIntMax)
     return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  // the kernels address one batch's Q / K / V rows with 32-bit byte offsets
+  if (S * Hq * D * 4 > kIntMax)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: one batch of Q or K/V exceeds 2 GiB", fn);
   return GSA_OK;
 }
 

@@ -38,10 +38,7 @@ constexpr int BN = 64;   // keys per tile
 
 enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2 };
 
-// Position of key offset `ko` (0..63) inside a Vᵀ row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int ko) {
-  return (ko & ~15) | ((ko & 4) << 1) | ((ko & 8) >> 1) | (ko & 3);
-}
+#define GSA_LDS __attribute__((address_space(3)))
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2)
@@ -50,13 +47,16 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
                           bf16* __restrict__ Y, int B, int S, int Hq, int Hkv, int n_qtiles,
                           float scale_log2) {
   using namespace fwd;
-  constexpr int KLD = D + 8;   // K tile row stride (bf16): 16-B aligned, 4-bank rotation per row
-  constexpr int VLD = BN + 8;  // Vᵀ tile row stride (bf16)
-  __shared__ __align__(16) bf16 Ks[2][BN * KLD];
-  __shared__ __align__(16) bf16 Vt[2][D * VLD];
+  constexpr int CH = D / 8;       // 16-byte chunks per K/V row
+  constexpr int KSL = CH + 1;     // K row stride in 16-B slots (one pad slot: 4-bank rotation per row)
+  constexpr int VSL = CH;         // V rows are unpadded, chunk-swizzled
+  constexpr int VSW = CH / 4 - 1; // V swizzle: chunk ^= 4 * (row & VSW)
+  __shared__ __align__(16) bf16 Ks[2][BN * KSL * 8];
+  __shared__ __align__(16) bf16 Vs[2][BN * VSL * 8];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int l32 = lane & 31, hl = lane >> 5;
 
   // heaviest (last) query tiles first, then heads, then batches
@@ -77,16 +77,14 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const bf16* Kb = K + (int64_t)b * S * kv_row + (int64_t)kvh * D;
   const bf16* Vb = V + (int64_t)b * S * kv_row + (int64_t)kvh * D;
 
-  // Q fragments: B operand of Sᵀ = K·Qᵀ, lane holds Q[my_q][16*kk + 8*hl .. +7]
+  // Q fragments: B operand of Sᵀ = K·Qᵀ, lane holds Q[my_q][16*kk + 8*hl .. +7];
+  // rows past the end read zeros (buffer range check) and are never stored
   bf16x8 qf[D / 16];
+  {
+    const auto qr = make_rsrc(Qb, (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2));
+    const uint32_t qo = (uint32_t)(((int64_t)my_q * q_row + 8 * hl) * 2);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (my_q < S) {
-      qf[kk] = *(const bf16x8*)(Qb + (int64_t)my_q * q_row + 16 * kk + 8 * hl);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (bf16)0.0f;
-    }
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(qr, qo + 32 * kk, 0));
   }
 
   f32x16 o[D / 32];
@@ -94,133 +92,205 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  // m_run is the reference max of the exp2-domain scores: it only moves when a
+  // row's max grows by more than kRescale (then O and l are rescaled), so p may
+  // reach 2^kRescale.  O/l does not depend on the reference (exact in real
+  // arithmetic); a row's first tile always sets it.
+  constexpr float kRescale = 8.0f;
   float m_run = -INFINITY, l_run = 0.f;
 
   const int kv_end = min(S, q0 + BM);
   const int n_kv = ceil_div(kv_end, BN);
 
-  // K loader: KCH 16-B chunks per row, KRP rows per pass
-  constexpr int KCH = D / 8, KRP = 256 / KCH, KPASS = BN / KRP;
-  // V loader: VKR consecutive keys × 8 dims per thread
-  constexpr int VKR = BN * D / (256 * 8), VKG = BN / VKR;
-  const int k_row = tid / KCH, k_ch = tid % KCH;
-  const int v_kg = tid % VKG, v_dg = tid / VKG;
-  u32x4 kreg[KPASS], vreg[VKR];
-
-  auto load_kv = [&](int k0) {
+  // ---- global -> LDS: 16-byte direct loads (buffer_load ... lds); lane l of a
+  // wave instruction lands in slot (instruction base + l).  Keys >= S read as
+  // zeros (range check; the whole offset is in the VGPR) and are masked later.
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)S * kv_row - (int64_t)kvh * D) * 2);
+  const auto krs = make_rsrc(Kb, kv_bytes);
+  const auto vrs = make_rsrc(Vb, kv_bytes);
+  const uint32_t row_b = (uint32_t)(kv_row * 2);
+  // K slot s = row*KSL + chunk (chunk CH is padding: loads from past the end -> 0)
+  uint32_t k_off[(KSL + 3) / 4];
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int key = k0 + k_row + p * KRP;
-      kreg[p] = key < S ? *(const u32x4*)(Kb + (int64_t)key * kv_row + k_ch * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int j = 0; j < (KSL + 3) / 4; ++j) {
+    const int sl = (wave + 4 * j) * 64 + lane;
+    const int row = sl / KSL, ch = sl % KSL;
+    k_off[j] = ch < CH ? (uint32_t)row * row_b + ch * 16 : 0xfffffff0u;
+  }
+  // V slot s = row*VSL + phys; phys = chunk ^ 4*(row & VSW)
+  uint32_t v_off[VSL / 4];
 #pragma unroll
-    for (int r = 0; r < VKR; ++r) {
-      const int key = k0 + v_kg * VKR + r;
-      vreg[r] = key < S ? *(const u32x4*)(Vb + (int64_t)key * kv_row + v_dg * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_kv = [&](int buf) {
+  for (int j = 0; j < VSL / 4; ++j) {
+    const int sl = (wave + 4 * j) * 64 + lane;
+    const int row = sl / VSL, phys = sl % VSL;
+    v_off[j] = (uint32_t)row * row_b + (uint32_t)((phys ^ (4 * (row & VSW))) * 16);
+  }
+  auto dma_k = [&](int k0, int buf) {
+    const uint32_t base = (uint32_t)k0 * row_b;
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p)
-      *(u32x4*)(&Ks[buf][(k_row + p * KRP) * KLD + k_ch * 8]) = kreg[p];
-    const int pos = vt_pos(v_kg * VKR);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      bf16* dst = &Vt[buf][(v_dg * 8 + e) * VLD + pos];
-      if constexpr (VKR == 4) {
-        const uint32_t h0 = (vreg[0][w] >> sh) & 0xffffu, h1 = (vreg[1][w] >> sh) & 0xffffu;
-        const uint32_t h2 = (vreg[2][w] >> sh) & 0xffffu, h3 = (vreg[3][w] >> sh) & 0xffffu;
-        *(u32x2*)dst = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
-      } else {
-        const uint32_t h0 = (vreg[0][w] >> sh) & 0xffffu, h1 = (vreg[1][w] >> sh) & 0xffffu;
-        *(uint32_t*)dst = h0 | (h1 << 16);
+    for (int j = 0; j < (KSL + 3) / 4; ++j) {
+      const int ins = wave + 4 * j;
+      if (ins < KSL) {
+        const uint32_t off = k_off[j] == 0xfffffff0u ? 0xfffffff0u : k_off[j] + base;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (GSA_LDS void*)&Ks[buf][ins * 64 * 8], 16, (int)off, 0, 0, 0);
       }
     }
   };
-
-  const bool wave_rows_valid = qw0 < S;
-
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
-  for (int it = 0; it < n_kv; ++it) {
-    const int buf = it & 1;
-    const int k0 = it * BN;
-    if (it + 1 < n_kv) load_kv(k0 + BN);
-
-    // a wave whose rows all precede this tile's first key has nothing to do
-    if (wave_rows_valid && k0 <= qw0 + 31) {
-      f32x16 s[2];
+  auto dma_v = [&](int k0, int buf) {
+    const uint32_t base = (uint32_t)k0 * row_b;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+    for (int j = 0; j < VSL / 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (GSA_LDS void*)&Vs[buf][(wave + 4 * j) * 64 * 8], 16,
+                                               (int)(v_off[j] + base), 0, 0, 0);
+  };
+
+  // ---- LDS -> MFMA operands
+  // K (A operand of Sᵀ): lane reads row sub*32 + l32, chunk 2*kk + hl (one 16-B read)
+  const bf16* ks_rd = &Ks[0][(l32 * KSL + hl) * 8];
+  // Vᵀ (A operand of Oᵀ += Vᵀ·Pᵀ) via transposed 8-byte reads.  In a 16-lane group
+  // g = lane/16, lane i names row 4*(g/2) + i/4 (+ 8*a + 16*t + 32*sub) and dims
+  // dt*32 + 16*(g%2) + 4*(i%4) .. +3; the read hands lane i the four rows' values
+  // at dim dt*32 + 16*(g%2) + i, i.e. MFMA row l32, k slots 4a..4a+3 = keys
+  // 16t + 8a + 4*hl + 0..3 of the subtile, matching the P layout.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int v_r = 4 * (vg >> 1) + (vi >> 2);           // row within a 16-key block (and r & 3 == vi >> 2)
+  const int v_dc = 16 * (vg & 1) + 4 * (vi & 3);       // dim offset within a 32-dim block
+  uint32_t vt_base[D / 32];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int chunk = dt * 4 + (v_dc >> 3);
+    const int phys = chunk ^ (4 * (v_r & VSW));
+    vt_base[dt] = (uint32_t)(v_r * VSL * 16 + phys * 16 + (v_dc & 7) * 2);
+  }
+  const uint32_t vs_lds0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Vs[0][0];
+
+  // Sᵀ tile (64 keys x this wave's 32 rows) from the K tile in buffer kb
+  auto mma_s = [&](int kb, f32x16 (&s)[2]) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(&Ks[buf][(sub * 32 + l32) * KLD + 16 * kk + 8 * hl]);
-          s[sub] = mfma32x32x16(a, qf[kk], s[sub]);
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(ks_rd + kb * (BN * KSL * 8) + (sub * 32 * KSL + 2 * kk) * 8);
+        s[sub] = mfma32x32x16(a, qf[kk], s[sub]);
+      }
+    }
+  };
+  // Oᵀ += Vᵀ·Pᵀ from the V tile in buffer vb
+  auto mma_pv = [&](int vb, const bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t a0 = vs_lds0 + vb * (BN * VSL * 16) + vt_base[dt] + (sub * 32 + 16 * t) * VSL * 16;
+          const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)a0);
+          const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)(a0 + 8 * VSL * 16));
+          bf16x8 a;
+          a.lo = __builtin_bit_cast(bf16x4, lo);
+          a.hi = __builtin_bit_cast(bf16x4, hi);
+          o[dt] = mfma32x32x16(a, pb[sub][t], o[dt]);
         }
-      }
-      // scale into the log2 domain and apply the causal / length mask
-      const bool need_mask = (k0 + BN - 1 > qw0) || (k0 + BN > S);
-      float mx = -INFINITY;
+  };
+  // Online softmax of one Sᵀ tile: scale into the log2 domain, optional
+  // causal/length mask, row max (in-lane, then across the two wave halves),
+  // reference update, p = exp2(t - m), row sum folded into l, P packed to bf16.
+  // Returns whether any lane moved its reference (O must then be scaled by alpha).
+  float alpha = 1.f;
+  auto softmax = [&](f32x16 (&s)[2], bool masked, int k0, bf16x8 (&pb)[2][2]) -> bool {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] *= scale_log2;
+    if (masked) {
+      // key offset within the tile of element (sub, r): sub*32 + 8*(r/4) + 4*hl + r%4
+      const int lim = min(my_q, S - 1) - k0 - 4 * hl;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t = s[sub][r] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key > my_q || key >= S) t = -INFINITY;
-          }
-          s[sub][r] = t;
-          mx = fmaxf(mx, t);
+          const int off = sub * 32 + 8 * (r >> 2) + (r & 3);
+          s[sub][r] = off <= lim ? s[sub][r] : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float ps = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[sub][r] - m_new);
-          s[sub][r] = p;
-          ps += p;
-        }
-      l_run = l_run * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[sub][t][e] = (bf16)s[sub][8 * t + e];
-
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16x8 a = *(const bf16x8*)(&Vt[buf][(dt * 32 + l32) * VLD + sub * 32 + 16 * t + 8 * hl]);
-            o[dt] = mfma32x32x16(a, pb[sub][t], o[dt]);
-          }
     }
-
-    if (it + 1 < n_kv) store_kv(buf ^ 1);
+    float mx = s[0][0];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    {
+      // max with the other wave half (same query row, the other 32 keys)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    }
+    // move the reference only when the max grew by more than kRescale
+    // (always on a row's first tile, where m_run = -inf)
+    const bool move = mx > m_run + kRescale;
+    const float m_new = move ? mx : m_run;
+    alpha = fast_exp2(m_run - m_new);   // 1 when not moving, 0 on the first tile
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[sub][r] = fast_exp2(s[sub][r] - m_new);
+        ps += s[sub][r];
+      }
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[sub][t][e] = (bf16)s[sub][8 * t + e];
+    return __any(move);
+  };
+  auto rescale_o = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+  };
+  auto wait_dma_and_sync = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  // Pipeline: K runs one tile ahead of V.  At the top of iteration t, K buffer
+  // (t+1)&1 holds K(t+1), V buffer t&1 holds V(t) and `cur` holds Sᵀ(t).  The
+  // direct loads of K(t+2) and V(t+1) go to K buffer t&1 and V buffer (t+1)&1,
+  // both last read in iteration t-1, and are waited for before the barrier.
+  // Sᵀ(t+1) runs on the matrix cores while the VALU works on softmax(t).
+  auto step = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int k0 = it * BN;
+    const bool has_next = it + 1 < n_kv;
+    if (it + 2 < n_kv) dma_k(k0 + 2 * BN, it & 1);
+    if (has_next) dma_v(k0 + BN, (it + 1) & 1);
+    if (has_next) mma_s((it + 1) & 1, nxt);
+    const bool masked = (k0 + BN - 1 > qw0) || (k0 + BN > S);
+    bf16x8 pb[2][2];
+    if (softmax(cur, masked, k0, pb)) rescale_o();
+    mma_pv(it & 1, pb);
+    wait_dma_and_sync();
+  };
+
+  f32x16 sA[2], sB[2];
+  dma_k(0, 0);
+  dma_v(0, 0);
+  if (n_kv > 1) dma_k(BN, 1);
+  wait_dma_and_sync();
+  mma_s(0, sA);
+  __syncthreads();   // K buffer 0 is refilled in the first iteration
+  for (int it = 0; it < n_kv; it += 2) {
+    step(it, sA, sB);
+    if (it + 1 < n_kv) step(it + 1, sB, sA);
   }
 
   if (my_q >= S) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);  // the two halves summed different keys
   const float inv = 1.0f / l_tot;
   const int64_t tok = (int64_t)b * S + my_q;
   bf16* yrow = Y + tok * q_row + (int64_t)head * D;
