@@ -138,6 +138,264 @@ void gate_gemm_bf16_kernel(const bf16* __restrict__ X, const bf16* __restrict__ 
     }
 }
 
+#define GSA_LDS __attribute__((address_space(3)))
+
+// Large-tile bf16 gate projection: a 256×256 output tile per 512-thread
+// workgroup (8 waves as 2 (M) × 4 (N), each 128×64 = 4×2 MFMA 32x32x16 tiles),
+// K staged 64 at a time, double-buffered.  X and W tiles move global -> LDS
+// with 16-byte direct loads (buffer_load ... lds; lane l of an instruction lands
+// in slot base + l), so no registers or VALU work are spent staging them.
+//   X tile: 256 rows × 8 chunks + 1 pad slot (144-B row stride); the MFMA A
+//           operand (row m, 8 consecutive k) is one 16-B read.
+//   W tile: 64 rows (k) × 32 chunks (512 B), chunk index XOR 4*(k & 3); the
+//           MFMA B operand (column n, 8 consecutive k) comes from two
+//           transposed reads (ds_read_b64_tr_b16), 4 k values each.
+// Workgroups are mapped so that each XCD (workgroup id mod 8) owns a
+// contiguous range of M tiles: an X row block is fetched into one L2 only.
+// The k order of every output's sum (16-wide MFMA steps, increasing k, one
+// accumulator) is the same as in the narrow kernel below, so both produce
+// bitwise identical scores.
+namespace gemm_big {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int XSL = BK / 8 + 1;   // 9 slots per X row
+constexpr int WSL = BN / 8;       // 32 slots per W row
+constexpr uint32_t kOOB = 0xfffffff0u;  // an offset past any buffer: reads zeros
+}  // namespace gemm_big
+
+__global__ __launch_bounds__(512, 1)
+void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
+                               float* __restrict__ G, int M, int K, int N, int tiles_m, int tiles_n,
+                               int apply_sigmoid) {
+  using namespace gemm_big;
+  __shared__ __align__(16) bf16 Xs[2][BM * XSL * 8];
+  __shared__ __align__(16) bf16 Ws[2][BK * WSL * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  // tile index: XCD x = bid % 8 takes the x-th contiguous eighth of the
+  // row-major tile list when the tile count divides evenly
+  const int T = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  const int tm = t / tiles_n, tn = t % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const auto xr = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
+  const auto wr = make_rsrc(W, (uint32_t)((int64_t)K * N * 2));
+
+  // per-lane DMA offsets (the K-step base is added per stage)
+  constexpr int XINS = BM * XSL / 64;          // 36 X instructions per stage
+  constexpr int XPW = (XINS + 7) / 8;          // per wave (5; the last round is partial)
+  uint32_t x_off[XPW];
+  int x_kc[XPW];
+#pragma unroll
+  for (int j = 0; j < XPW; ++j) {
+    const int sl = (wave + 8 * j) * 64 + lane;
+    const int row = sl / XSL, c = sl % XSL;
+    x_kc[j] = c < 8 ? c * 8 : 1 << 30;       // k offset of this chunk within the stage
+    x_off[j] = (uint32_t)(m0 + row) * (uint32_t)K * 2 + (uint32_t)(c * 16);
+  }
+  constexpr int WINS = BK * WSL / 64;          // 32 W instructions per stage
+  uint32_t w_off[WINS / 8];
+#pragma unroll
+  for (int j = 0; j < WINS / 8; ++j) {
+    const int sl = (wave + 8 * j) * 64 + lane;
+    const int row = sl / WSL, p = sl % WSL;
+    const int c = p ^ (4 * (row & 3));
+    w_off[j] = (uint32_t)row * (uint32_t)N * 2 + (uint32_t)(n0 + 8 * c) * 2;
+  }
+  auto dma = [&](int k0, int buf) {
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      const int ins = wave + 8 * j;
+      if (ins < XINS) {
+        const uint32_t off = (k0 + x_kc[j] < K) ? x_off[j] + (uint32_t)k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (GSA_LDS void*)&Xs[buf][ins * 64 * 8], 16, (int)off, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WINS / 8; ++j) {
+      const int ins = wave + 8 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (GSA_LDS void*)&Ws[buf][ins * 64 * 8], 16,
+                                               (int)(w_off[j] + (uint32_t)k0 * (uint32_t)N * 2), 0, 0, 0);
+    }
+  };
+
+  // operand addresses
+  const bf16* xa = &Xs[0][((wm * 128 + l32) * XSL + hl) * 8];
+  const int g = lane >> 4, si = lane & 15;
+  // B: supplier lane (g, si) names k row 8*(g/2) + si/4 (+4a +16kk) and columns
+  // wn*64 + nt*32 + 16*(g%2) + 4*(si%4) .. +3
+  uint32_t wb[2];
+  const uint32_t ws0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Ws[0][0];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = wn * 64 + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
+    const int krow = 8 * (g >> 1) + (si >> 2);
+    const int phys = (n >> 3) ^ (4 * (krow & 3));
+    wb[nt] = ws0 + (uint32_t)((krow * WSL + phys) * 16 + (n & 7) * 2);
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (K + BK - 1) / BK;
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) dma((kt + 1) * BK, buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        a[mt] = *(const bf16x8*)(xa + buf * (BM * XSL * 8) + (mt * 32 * XSL + 2 * kk) * 8);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t ad = wb[nt] + (uint32_t)buf * (BK * WSL * 16) + (uint32_t)(16 * kk * WSL * 16);
+        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)ad);
+        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)(ad + 4 * WSL * 16));
+        b[nt].lo = __builtin_bit_cast(bf16x4, lo);
+        b[nt].hi = __builtin_bit_cast(bf16x4, hi);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[mt], b[nt], acc[mt][nt]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = n0 + wn * 64 + nt * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (m < M && n < N) {
+          const float z = acc[mt][nt][r];
+          G[(int64_t)m * N + n] = apply_sigmoid ? sigmoidf(z) : z;
+        }
+      }
+    }
+}
+
+// Narrow / short bf16 gate projection for shapes with few rows (decode: one
+// token per batch) or few columns (headwise gate: one per head): each
+// single-wave workgroup owns one 32×32 output tile and streams the whole K
+// through an 8-stage ring of LDS buffers filled by 16-byte direct loads, so up
+// to 7 stages (56 KB) are in flight per wave.  No barrier is needed: a wave
+// only reads what its own loads wrote, after waiting on them.
+//   X stage: 32 rows × 8 chunks (k 64), chunk index XOR (row & 7); the A
+//            operand is one 16-B read.
+//   W stage: 64 rows (k) × 4 chunks (32 columns, 64 B), unswizzled (eight
+//            consecutive rows are 512 contiguous bytes); the B operand comes
+//            from two transposed reads.
+namespace gemm_narrow {
+constexpr int BK = 64, NS = 8;
+constexpr int XSLOTS = 32 * 8, WSLOTS = 64 * 4;     // 16-B slots per stage
+constexpr uint32_t kOOB = 0xfffffff0u;
+}  // namespace gemm_narrow
+
+__global__ __launch_bounds__(64)
+void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
+                                  float* __restrict__ G, int M, int K, int N, int tiles_n,
+                                  int apply_sigmoid) {
+  using namespace gemm_narrow;
+  __shared__ __align__(16) bf16 Xs[NS][XSLOTS * 8];
+  __shared__ __align__(16) bf16 Ws[NS][WSLOTS * 8];
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * 32, n0 = tn * 32;
+
+  const auto xr = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
+  const auto wr = make_rsrc(W, (uint32_t)((int64_t)K * N * 2));
+  // DMA slots: X instruction i covers rows 8i .. 8i+7; W instruction i rows 16i .. 16i+15
+  uint32_t x_off[4], w_off[4];
+  int x_k[4], w_n[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sl = i * 64 + lane;
+    const int row = sl >> 3, p = sl & 7;
+    const int c = p ^ (row & 7);
+    x_k[i] = c * 8;
+    x_off[i] = (uint32_t)(m0 + row) * (uint32_t)K * 2 + (uint32_t)(c * 16);
+    const int krow = sl >> 2, wc = sl & 3;
+    w_n[i] = n0 + wc * 8;
+    w_off[i] = (uint32_t)krow * (uint32_t)N * 2 + (uint32_t)(n0 + wc * 8) * 2;
+  }
+  const bool n_ok = (N % 8) == 0;
+  auto dma = [&](int k0, int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (k0 + x_k[i] < K) ? x_off[i] + (uint32_t)k0 * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (GSA_LDS void*)&Xs[st][i * 64 * 8], 16, (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (n_ok && w_n[i] < N) ? w_off[i] + (uint32_t)k0 * (uint32_t)N * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (GSA_LDS void*)&Ws[st][i * 64 * 8], 16, (int)off, 0, 0, 0);
+    }
+  };
+
+  // A operand: row l32, chunk 2*kk + hl, stored at chunk ^ (l32 & 7)
+  const uint32_t xs0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Xs[0][0];
+  const uint32_t ws0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Ws[0][0];
+  // B operand: supplier lane (g, si) names k row 8*(g/2) + si/4 (+4a +16kk) and
+  // columns 16*(g%2) + 4*(si%4) .. +3 of the 32-column stage
+  const int g = lane >> 4, si = lane & 15;
+  const uint32_t wb = ws0 + (uint32_t)(((8 * (g >> 1) + (si >> 2)) * 4) * 16 + (16 * (g & 1) + 4 * (si & 3)) * 2);
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int nk = (K + BK - 1) / BK;
+  // prologue: stages 0 .. NS-2 in flight
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) dma(st * BK, st);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % NS;
+    if (kt + NS - 1 < nk) {
+      dma((kt + NS - 1) * BK, (kt + NS - 1) % NS);
+      asm volatile("s_waitcnt vmcnt(56)" ::: "memory");   // the 7 newer stages (8 loads each) may still fly
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = 2 * kk + hl;
+      const bf16x8 a = *(const bf16x8*)(GSA_LDS bf16x8*)(uintptr_t)(xs0 + st * (XSLOTS * 16) +
+                                                                    (l32 * 8 + (c ^ (l32 & 7))) * 16);
+      const uint32_t ad = wb + st * (WSLOTS * 16) + 16 * kk * 4 * 16;
+      bf16x8 b;
+      b.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)ad));
+      b.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)(ad + 4 * 4 * 16)));
+      acc = mfma32x32x16(a, b, acc);
+    }
+  }
+  const int n = n0 + l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (m < M && n < N) G[(int64_t)m * N + n] = apply_sigmoid ? sigmoidf(acc[r]) : acc[r];
+  }
+}
+
 // float32 gate projection: 64×64 tile per 256 threads, 4×4 outputs per thread.
 __global__ __launch_bounds__(256)
 void gate_gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__ W,
@@ -186,7 +444,20 @@ void gate_gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__
 
 hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, int64_t K, int64_t N,
                             bool bf16_inputs, bool apply_sigmoid, hipStream_t stream) {
-  if (bf16_inputs) {
+  if (bf16_inputs && M >= 256 && N >= 256 && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) &&
+      K * N * 2 < (int64_t(1) << 31)) {
+    const int tiles_n = (int)ceil_div<int64_t>(N, gemm_big::BN);
+    const int tiles_m = (int)ceil_div<int64_t>(M, gemm_big::BM);
+    hipLaunchKernelGGL(gate_gemm_bf16_big_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
+                       (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_m, tiles_n,
+                       (int)apply_sigmoid);
+  } else if (bf16_inputs && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) && K * N * 2 < (int64_t(1) << 31)) {
+    const int tiles_n = (int)ceil_div<int64_t>(N, 32);
+    const int64_t tiles = ceil_div<int64_t>(M, 32) * tiles_n;
+    hipLaunchKernelGGL(gate_gemm_bf16_narrow_kernel, dim3((unsigned)tiles), dim3(64), 0, stream,
+                       (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_n,
+                       (int)apply_sigmoid);
+  } else if (bf16_inputs) {
     const int tiles_n = (int)ceil_div<int64_t>(N, gemm::BN);
     const int64_t tiles = ceil_div<int64_t>(M, gemm::BM) * tiles_n;
     hipLaunchKernelGGL(gate_gemm_bf16_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
