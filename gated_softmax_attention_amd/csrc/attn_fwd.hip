@@ -27,6 +27,8 @@
 //              permuted inside each 16-key block (offset bits 2 and 3 swapped)
 //              so each lane's 8 keys are one 16-byte LDS read.
 // Epilogue: O/l, times the float32 gate, one round-to-nearest-even to bf16.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gsa {
@@ -51,8 +53,13 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   constexpr int KSL = CH + 1;     // K row stride in 16-B slots (one pad slot: 4-bank rotation per row)
   constexpr int VSL = CH;         // V rows are unpadded, chunk-swizzled
   constexpr int VSW = CH / 4 - 1; // V swizzle: chunk ^= 4 * (row & VSW)
-  __shared__ __align__(16) bf16 Ks[2][BN * KSL * 8];
-  __shared__ __align__(16) bf16 Vs[2][BN * VSL * 8];
+  // one LDS object per stage: the compiler's alias information then knows a
+  // direct load into one stage cannot touch the other, and does not make reads
+  // of the current stage wait for loads still filling the next one
+  __shared__ __align__(16) bf16 Ks0[BN * KSL * 8];
+  __shared__ __align__(16) bf16 Ks1[BN * KSL * 8];
+  __shared__ __align__(16) bf16 Vs0[BN * VSL * 8];
+  __shared__ __align__(16) bf16 Vs1[BN * VSL * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,28 +132,28 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const int row = sl / VSL, phys = sl % VSL;
     v_off[j] = (uint32_t)row * row_b + (uint32_t)((phys ^ (4 * (row & VSW))) * 16);
   }
-  auto dma_k = [&](int k0, int buf) {
+  auto dma_k = [&](int k0, bf16* kdst) {
     const uint32_t base = (uint32_t)k0 * row_b;
 #pragma unroll
     for (int j = 0; j < (KSL + 3) / 4; ++j) {
       const int ins = wave + 4 * j;
       if (ins < KSL) {
         const uint32_t off = k_off[j] == 0xfffffff0u ? 0xfffffff0u : k_off[j] + base;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (GSA_LDS void*)&Ks[buf][ins * 64 * 8], 16, (int)off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (GSA_LDS void*)&kdst[ins * 64 * 8], 16, (int)off, 0, 0, 0);
       }
     }
   };
-  auto dma_v = [&](int k0, int buf) {
+  auto dma_v = [&](int k0, bf16* vdst) {
     const uint32_t base = (uint32_t)k0 * row_b;
 #pragma unroll
     for (int j = 0; j < VSL / 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (GSA_LDS void*)&Vs[buf][(wave + 4 * j) * 64 * 8], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (GSA_LDS void*)&vdst[(wave + 4 * j) * 64 * 8], 16,
                                                (int)(v_off[j] + base), 0, 0, 0);
   };
 
   // ---- LDS -> MFMA operands
   // K (A operand of Sᵀ): lane reads row sub*32 + l32, chunk 2*kk + hl (one 16-B read)
-  const bf16* ks_rd = &Ks[0][(l32 * KSL + hl) * 8];
+  const int ks_lane = (l32 * KSL + hl) * 8;
   // Vᵀ (A operand of Oᵀ += Vᵀ·Pᵀ) via transposed 8-byte reads.  In a 16-lane group
   // g = lane/16, lane i names row 4*(g/2) + i/4 (+ 8*a + 16*t + 32*sub) and dims
   // dt*32 + 16*(g%2) + 4*(i%4) .. +3; the read hands lane i the four rows' values
@@ -162,32 +169,37 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const int phys = chunk ^ (4 * (v_r & VSW));
     vt_base[dt] = (uint32_t)(v_r * VSL * 16 + phys * 16 + (v_dc & 7) * 2);
   }
-  const uint32_t vs_lds0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Vs[0][0];
 
-  // Sᵀ tile (64 keys x this wave's 32 rows) from the K tile in buffer kb
-  auto mma_s = [&](int kb, f32x16 (&s)[2]) {
+  // Sᵀ tile (64 keys x this wave's 32 rows) from the K tile at ksrc; the two
+  // 32-key halves are independent accumulation chains, interleaved
+  auto mma_s = [&](const bf16* ksrc, f32x16 (&s)[2]) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(ks_rd + kb * (BN * KSL * 8) + (sub * 32 * KSL + 2 * kk) * 8);
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 a = *(const bf16x8*)(ksrc + ks_lane + (sub * 32 * KSL + 2 * kk) * 8);
         s[sub] = mfma32x32x16(a, qf[kk], s[sub]);
       }
-    }
   };
-  // Oᵀ += Vᵀ·Pᵀ from the V tile in buffer vb
-  auto mma_pv = [&](int vb, const bf16x8 (&pb)[2][2]) {
+  // Oᵀ += Vᵀ·Pᵀ from the V tile at vsrc; the D/32 output blocks are
+  // independent accumulation chains, interleaved
+  auto mma_pv = [&](const bf16* vsrc, const bf16x8 (&pb)[2][2]) {
+    // an LDS pointer derived from the stage array (not from an integer), so
+    // the compiler keeps the provenance it needs for its alias information
+    GSA_LDS char* const vs = (GSA_LDS char*)(GSA_LDS void*)vsrc;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t a0 = vs_lds0 + vb * (BN * VSL * 16) + vt_base[dt] + (sub * 32 + 16 * t) * VSL * 16;
-          const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)a0);
-          const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)(a0 + 8 * VSL * 16));
+        for (int dt = 0; dt < D / 32; ++dt) {
+          GSA_LDS char* const a0 = vs + vt_base[dt] + (sub * 32 + 16 * t) * VSL * 16;
+          const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)a0);
+          const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(a0 + 8 * VSL * 16));
           bf16x8 a;
           a.lo = __builtin_bit_cast(bf16x4, lo);
           a.hi = __builtin_bit_cast(bf16x4, hi);
@@ -264,29 +276,35 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // direct loads of K(t+2) and V(t+1) go to K buffer t&1 and V buffer (t+1)&1,
   // both last read in iteration t-1, and are waited for before the barrier.
   // Sᵀ(t+1) runs on the matrix cores while the VALU works on softmax(t).
-  auto step = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  // iteration `it` with compile-time buffer parity P = it & 1
+  auto step = [&](auto parity, int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr int P = decltype(parity)::value;
+    bf16* const k_cur = P ? Ks1 : Ks0;   // held K(t), consumed in iteration t-1: refill with K(t+2)
+    bf16* const k_nxt = P ? Ks0 : Ks1;   // K(t+1)
+    bf16* const v_cur = P ? Vs1 : Vs0;   // V(t)
+    bf16* const v_nxt = P ? Vs0 : Vs1;   // refill with V(t+1)
     const int k0 = it * BN;
     const bool has_next = it + 1 < n_kv;
-    if (it + 2 < n_kv) dma_k(k0 + 2 * BN, it & 1);
-    if (has_next) dma_v(k0 + BN, (it + 1) & 1);
-    if (has_next) mma_s((it + 1) & 1, nxt);
+    if (it + 2 < n_kv) dma_k(k0 + 2 * BN, k_cur);
+    if (has_next) dma_v(k0 + BN, v_nxt);
+    if (has_next) mma_s(k_nxt, nxt);
     const bool masked = (k0 + BN - 1 > qw0) || (k0 + BN > S);
     bf16x8 pb[2][2];
     if (softmax(cur, masked, k0, pb)) rescale_o();
-    mma_pv(it & 1, pb);
+    mma_pv(v_cur, pb);
     wait_dma_and_sync();
   };
 
   f32x16 sA[2], sB[2];
-  dma_k(0, 0);
-  dma_v(0, 0);
-  if (n_kv > 1) dma_k(BN, 1);
+  dma_k(0, Ks0);
+  dma_v(0, Vs0);
+  if (n_kv > 1) dma_k(BN, Ks1);
   wait_dma_and_sync();
-  mma_s(0, sA);
+  mma_s(Ks0, sA);
   __syncthreads();   // K buffer 0 is refilled in the first iteration
   for (int it = 0; it < n_kv; it += 2) {
-    step(it, sA, sB);
-    if (it + 1 < n_kv) step(it + 1, sB, sA);
+    step(std::integral_constant<int, 0>{}, it, sA, sB);
+    if (it + 1 < n_kv) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
   }
 
   if (my_q >= S) return;
