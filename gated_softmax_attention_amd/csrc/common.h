@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace gsa {
 
 typedef __bf16 bf16;
@@ -54,6 +57,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+// 16-byte direct global -> LDS load (buffer_load_dwordx4 ... lds): lane l's 16
+// bytes land at LDS address lds_addr + 16*l; offsets past the buffer's range
+// read as zeros.  Issued through inline assembly so the compiler does not
+// track it as a pending LDS write (it would otherwise make every later LDS
+// read wait for all such loads, even ones filling a different stage): the
+// caller waits for these loads itself (s_waitcnt vmcnt) before the barrier
+// that publishes the stage.  lds_addr must be wave-uniform.  Kernels using it
+// make no other use of m0.
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1, so
+// register-resident arrays are only ever indexed by constants.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <typename T>

@@ -208,35 +208,35 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
     w_off[j] = (uint32_t)row * (uint32_t)N * 2 + (uint32_t)(n0 + 8 * c) * 2;
   }
   auto dma = [&](int k0, int buf) {
+    const uint32_t xd = __builtin_amdgcn_readfirstlane(lds_addr(&Xs[buf][0]));
+    const uint32_t wd = __builtin_amdgcn_readfirstlane(lds_addr(&Ws[buf][0]));
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
       const int ins = wave + 8 * j;
       if (ins < XINS) {
         const uint32_t off = (k0 + x_kc[j] < K) ? x_off[j] + (uint32_t)k0 * 2 : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (GSA_LDS void*)&Xs[buf][ins * 64 * 8], 16, (int)off, 0, 0, 0);
+        dma16_lds(xr, off, xd + ins * 64 * 16);
       }
     }
 #pragma unroll
     for (int j = 0; j < WINS / 8; ++j) {
       const int ins = wave + 8 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (GSA_LDS void*)&Ws[buf][ins * 64 * 8], 16,
-                                               (int)(w_off[j] + (uint32_t)k0 * (uint32_t)N * 2), 0, 0, 0);
+      dma16_lds(wr, w_off[j] + (uint32_t)k0 * (uint32_t)N * 2, wd + ins * 64 * 16);
     }
   };
 
   // operand addresses
-  const bf16* xa = &Xs[0][((wm * 128 + l32) * XSL + hl) * 8];
+  const int xa = ((wm * 128 + l32) * XSL + hl) * 8;
   const int g = lane >> 4, si = lane & 15;
   // B: supplier lane (g, si) names k row 8*(g/2) + si/4 (+4a +16kk) and columns
   // wn*64 + nt*32 + 16*(g%2) + 4*(si%4) .. +3
   uint32_t wb[2];
-  const uint32_t ws0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Ws[0][0];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int n = wn * 64 + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
     const int krow = 8 * (g >> 1) + (si >> 2);
     const int phys = (n >> 3) ^ (4 * (krow & 3));
-    wb[nt] = ws0 + (uint32_t)((krow * WSL + phys) * 16 + (n & 7) * 2);
+    wb[nt] = (uint32_t)((krow * WSL + phys) * 16 + (n & 7) * 2);
   }
 
   f32x16 acc[4][2];
@@ -247,34 +247,39 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  dma(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) dma((kt + 1) * BK, buf ^ 1);
+  // one K step from the stage (xs, ws): 4 x 2 MFMA tiles, 4 k-steps of 16
+  auto compute = [&](const bf16* xs, const bf16* ws) {
+    GSA_LDS char* const wl = (GSA_LDS char*)(GSA_LDS void*)ws;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 a[4], b[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *(const bf16x8*)(xa + buf * (BM * XSL * 8) + (mt * 32 * XSL + 2 * kk) * 8);
+      for (int mt = 0; mt < 4; ++mt) a[mt] = *(const bf16x8*)(xs + xa + (mt * 32 * XSL + 2 * kk) * 8);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint32_t ad = wb[nt] + (uint32_t)buf * (BK * WSL * 16) + (uint32_t)(16 * kk * WSL * 16);
-        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)ad);
-        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(uintptr_t)(ad + 4 * WSL * 16));
-        b[nt].lo = __builtin_bit_cast(bf16x4, lo);
-        b[nt].hi = __builtin_bit_cast(bf16x4, hi);
+        GSA_LDS char* const ad = wl + wb[nt] + 16 * kk * WSL * 16;
+        b[nt].lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)ad));
+        b[nt].hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(ad + 4 * WSL * 16)));
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[mt], b[nt], acc[mt][nt]);
     }
+  };
+  auto sync = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  dma(0, 0);
+  sync();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) dma((kt + 1) * BK, buf ^ 1);
+    compute(&Xs[buf][0], &Ws[buf][0]);
+    sync();
   }
 
 #pragma unroll
@@ -340,15 +345,17 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
   }
   const bool n_ok = (N % 8) == 0;
   auto dma = [&](int k0, int st) {
+    const uint32_t xd = __builtin_amdgcn_readfirstlane(lds_addr(&Xs[st][0]));
+    const uint32_t wd = __builtin_amdgcn_readfirstlane(lds_addr(&Ws[st][0]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (k0 + x_k[i] < K) ? x_off[i] + (uint32_t)k0 * 2 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (GSA_LDS void*)&Xs[st][i * 64 * 8], 16, (int)off, 0, 0, 0);
+      dma16_lds(xr, off, xd + i * 64 * 16);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (n_ok && w_n[i] < N) ? w_off[i] + (uint32_t)k0 * (uint32_t)N * 2 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (GSA_LDS void*)&Ws[st][i * 64 * 8], 16, (int)off, 0, 0, 0);
+      dma16_lds(wr, off, wd + i * 64 * 16);
     }
   };
 
