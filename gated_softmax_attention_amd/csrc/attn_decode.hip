@@ -7,14 +7,19 @@
 //
 // Split kernel: workgroup (split s, key/value head c, batch b, quad of query
 // heads) streams keys [s*chunk, (s+1)*chunk) of head c once and serves up to 4
-// query heads of c's group.  Each wave takes 16-key blocks; per block:
+// query heads of c's group.  The keys move global -> LDS in 64-key stages
+// (K and V, 32 KB for D = 128) through a ring of 4 stages filled by 16-byte
+// direct loads, so ~96 KB per workgroup stay in flight independent of the
+// register file.  Each wave takes 16 keys of a stage:
 //   S = Q·Kᵀ on v_mfma_f32_16x16x32_bf16 with the (≤4) query rows replicated
 //     over the 16 MFMA rows, so every lane ends up holding the 4 heads' scores
-//     for "its" key, and K goes from HBM straight into MFMA operand registers
-//     (16 B per lane, no LDS);
-//   block max over the 16 keys by lane exchanges, online rescale, p = exp2(t − m);
+//     for "its" key;
+//   block max over the 16 keys by DPP row exchanges, online rescale,
+//     p = exp2(t − m);
 //   O += p·V on the VALU, each lane accumulating its key's contribution for 32
 //     of the 128 dims (reduced over the 16 key lanes once, at the end).
+// LDS rows are 16-byte-chunk swizzled (chunk ^= key & 15) so the 16 keys a
+// wave reads at one chunk hit distinct banks.
 // The workgroup merges its 4 waves' (m, l, O) through LDS and writes one
 // float32 partial (O, m, l) per query head.  The merge kernel combines the
 // splits exactly: m* = max m_s, l* = Σ l_s 2^{m_s − m*}, O* = Σ O_s 2^{m_s − m*},
@@ -24,9 +29,33 @@
 namespace gsa {
 
 namespace dec {
-constexpr int KB = 16;          // keys per MFMA block
+constexpr int KB = 16;          // keys per MFMA block (one wave)
 constexpr int WAVES = 4;
+constexpr int TK = KB * WAVES;  // keys per LDS stage
+constexpr int NS = 4;           // LDS ring depth
 }  // namespace dec
+
+// max / sum over the 16 lanes of a DPP row (quad swaps, then half-row and row mirrors)
+__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
+  int v = __float_as_int(x);
+  switch (ctrl_sel) {
+    case 0: v = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); break;   // quad_perm(1,0,3,2)
+    case 1: v = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); break;   // quad_perm(2,3,0,1)
+    case 2: v = __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: v = __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(v);
+}
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x = fmaxf(x, dpp_f(x, i));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x += dpp_f(x, i);
+  return x;
+}
 
 enum : int { kDecGateNone = 0, kDecGateElem = 1, kDecGateHead = 2 };
 
@@ -42,7 +71,8 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
   __shared__ float sm_m[WAVES][4], sm_l[WAVES][4];
   __shared__ float sm_o[WAVES][4][D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kl = lane & 15, jg = lane >> 4;
   const int s = blockIdx.x;
   const int G = Hq / Hkv;
@@ -54,7 +84,6 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
 
   const int key_begin = s * chunk;
   const int key_end = min(L, key_begin + chunk);
-  const int n_blocks = ceil_div(key_end - key_begin, KB);
 
   const int64_t kv_row = (int64_t)Hkv * D;
   const bf16* Kb = Kc + (int64_t)b * L * kv_row + (int64_t)c * D;
@@ -68,6 +97,10 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
     const bf16* qp = Q + ((int64_t)b * Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qa[kk] = *(const bf16x8*)(qp + 32 * kk + 8 * jg);
+    // settle the Q loads here: the ring's direct loads are invisible to the
+    // compiler's counters, which would otherwise wait for all of them inside the loop
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qa[kk]));
   }
 
   float m_run[4], l_run[4], o[4][NKK][8];
@@ -81,42 +114,78 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
       for (int e = 0; e < 8; ++e) o[r][kk][e] = 0.f;
   }
 
-  u32x4 kreg[NKK], vreg[NKK];
-  auto load = [&](int blk) {
-    const int key = key_begin + blk * KB + kl;
+  // ---- LDS ring of NS stages, each K[TK][D] and V[TK][D], chunk-swizzled rows
+  constexpr int CHK = D / 8;                         // 16-byte chunks per row
+  constexpr int STG = TK * D;                        // bf16 per stage and tensor
+  __shared__ __align__(16) bf16 Ks[NS][STG];
+  __shared__ __align__(16) bf16 Vs[NS][STG];
+  constexpr int NI = TK * CHK / 64 / WAVES;          // direct loads per wave, stage and tensor
+  const uint32_t row_b = (uint32_t)(kv_row * 2);
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)L * kv_row - (int64_t)c * D) * 2);
+  const auto krs = make_rsrc(Kb, kv_bytes);          // keys >= L read as zeros
+  const auto vrs = make_rsrc(Vb, kv_bytes);
+  uint32_t dma_off[NI];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int64_t off = (int64_t)key * kv_row + 32 * kk + 8 * jg;
-      kreg[kk] = key < key_end ? *(const u32x4*)(Kb + off) : u32x4{0, 0, 0, 0};
-      vreg[kk] = key < key_end ? *(const u32x4*)(Vb + off) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < NI; ++i) {
+    const int sl = (wave + WAVES * i) * 64 + lane;
+    const int row = sl / CHK, phys = sl % CHK;
+    dma_off[i] = (uint32_t)row * row_b + (uint32_t)((phys ^ (row & (CHK - 1))) * 16);
+  }
+  const int nkeys = key_end - key_begin;
+  const int n_st = ceil_div(nkeys, TK);
+  auto dma = [&](int st) {
+    const int buf = st % NS;
+    const uint32_t base = (uint32_t)(key_begin + st * TK) * row_b;
+    const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[buf][0]));
+    const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[buf][0]));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t ins = (uint32_t)(wave + WAVES * i) * 64 * 16;
+      dma16_lds(krs, dma_off[i] + base, kd + ins);
+      dma16_lds(vrs, dma_off[i] + base, vd + ins);
     }
   };
+  // wait until at most n stages of this wave's loads are still in flight
+  auto wait_stages = [&](int n) {
+    if (n >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * 2 * NI) : "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NI) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // this lane's key row within a stage and its operand chunks
+  const int my_row = wave * KB + kl;
 
-  int blk = wave;
-  if (blk < n_blocks) load(blk);
-  for (; blk < n_blocks; blk += WAVES) {
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < n_st) dma(st);
+  for (int t = 0; t < n_st; ++t) {
+    wait_stages(min(NS - 2, n_st - 1 - t));
+    __syncthreads();                                 // stage t complete; stage t-1 free
+    if (t + NS - 1 < n_st) dma(t + NS - 1);
+    const int buf = t % NS;
+    const int key = key_begin + t * TK + my_row;
     u32x4 kcur[NKK], vcur[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) { kcur[kk] = kreg[kk]; vcur[kk] = vreg[kk]; }
-    if (blk + WAVES < n_blocks) load(blk + WAVES);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int ch = (4 * kk + jg) ^ (my_row & (CHK - 1));
+      kcur[kk] = *(const u32x4*)(&Ks[buf][my_row * D + ch * 8]);
+      vcur[kk] = *(const u32x4*)(&Vs[buf][my_row * D + ch * 8]);
+    }
 
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       sacc = mfma16x16x32(qa[kk], __builtin_bit_cast(bf16x8, kcur[kk]), sacc);
-    // sacc[r] = score of query slot r against key (key_begin + blk*16 + kl)
-    const int key = key_begin + blk * KB + kl;
-    float t[4], alpha[4];
+    // sacc[r] = score of query slot r against this lane's key
+    float tt[4], alpha[4], m_use[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      t[r] = key < key_end ? sacc[r] * scale_log2 : -INFINITY;
-      float mx = t[r];
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      mx = fmaxf(mx, __shfl_xor(mx, 8));
+      tt[r] = key < key_end ? sacc[r] * scale_log2 : -INFINITY;
+      const float mx = row16_max(tt[r]);
       const float m_new = fmaxf(m_run[r], mx);
-      alpha[r] = fast_exp2(m_run[r] - m_new);
+      // a wave whose keys so far are all masked keeps m = -inf; exponentiate
+      // against 0 then, so that alpha and p come out 0 rather than NaN
+      m_use[r] = m_new == -INFINITY ? 0.f : m_new;
+      alpha[r] = fast_exp2(m_run[r] - m_use[r]);
       m_run[r] = m_new;
     }
     float vf[NKK][8];
@@ -129,9 +198,9 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(t[r] - m_run[r]);
+      const float p = fast_exp2(tt[r] - m_use[r]);
       l_run[r] = l_run[r] * alpha[r] + p;
-      if (alpha[r] != 1.0f) {   // uniform across the wave: m_run is a block-wide max
+      if (alpha[r] != 1.0f) {   // uniform within a DPP row: m_run is the 16-key max
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -147,23 +216,11 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
   // reduce over the 16 key lanes (lanes with equal jg hold the same dims)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float lr = l_run[r];
-    lr += __shfl_xor(lr, 1);
-    lr += __shfl_xor(lr, 2);
-    lr += __shfl_xor(lr, 4);
-    lr += __shfl_xor(lr, 8);
-    l_run[r] = lr;
+    l_run[r] = row16_sum(l_run[r]);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = o[r][kk][e];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        o[r][kk][e] = v;
-      }
+      for (int e = 0; e < 8; ++e) o[r][kk][e] = row16_sum(o[r][kk][e]);
   }
   if (kl == 0) {
 #pragma unroll
