@@ -146,7 +146,8 @@ def decode_bench(args, torch, gsa, cfg):
     if torch.isnan(Y.float()).any():
         raise RuntimeError("NaN in decode output")
     nbytes = cfg.decode_bytes()
-    kv = nbytes["kv"] + nbytes["q"] + nbytes["y"]   # what the decode call itself must move
+    # what the decode call itself must move: the cache, q, the fp32 gate and y
+    kv = nbytes["kv"] + nbytes["q"] + cfg.B * cfg.N * 4 + nbytes["y"]
     achieved = kv / (dec_ms * 1e-3) / 1e9
     traffic = measured_traffic("decode_split", ["attn_decode.hip", "common.h"])
     return {
