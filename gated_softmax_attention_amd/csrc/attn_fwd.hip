@@ -18,9 +18,12 @@
 //              accumulator layout a lane owns ONE query and 16 keys, so the
 //              online-softmax max/sum are in-lane with a single exchange
 //              between the two wave halves.
-//   softmax    t = s·(log2 e/√D); m = max(m_old, max t); p = exp2(t − m), the
-//              same rounded t feeding both m and p (so a lone visible key gets
-//              p = 1 exactly); l accumulates p; O is rescaled by exp2(m_old − m).
+//   softmax    in the log2 domain: m = max(m_old, max(s)·(log2 e/√D)),
+//              p = exp2(s·(log2 e/√D) − m) as one fused multiply-add and one
+//              exp2 per score; l accumulates the bf16-rounded p, the same
+//              weights the PV product applies (so a lone visible key, whose p
+//              rounds to 1, yields exactly its value row); O is rescaled by
+//              exp2(m_old − m).
 //   Oᵀ += Vᵀ·Pᵀ on MFMA (A = Vᵀ rows from LDS, B = P rounded to bf16, taken
 //              straight from the Sᵀ accumulators).  The k order of this product
 //              follows the accumulator layout; the Vᵀ tile is stored with keys
@@ -32,6 +35,8 @@
 #include "common.h"
 
 namespace gsa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace fwd {
 constexpr int BM = 128;  // query rows per workgroup
@@ -132,8 +137,12 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const int row = sl / VSL, phys = sl % VSL;
     v_off[j] = (uint32_t)row * row_b + (uint32_t)((phys ^ (4 * (row & VSW))) * 16);
   }
-  auto dma_k = [&](int k0, bf16* kdst) {
-    const uint32_t base = (uint32_t)k0 * row_b;
+  // a tile that is not needed gets a base past the range check: its loads
+  // write zeros to LDS and never touch memory (offsets stay below 2^32:
+  // base 2^31 plus at most BN rows of at most 2^20 bytes)
+  constexpr uint32_t kNoTile = 0x80000000u;
+  auto dma_k = [&](int k0, bool need, bf16* kdst) {
+    const uint32_t base = need ? (uint32_t)k0 * row_b : kNoTile;
 #pragma unroll
     for (int j = 0; j < (KSL + 3) / 4; ++j) {
       const int ins = wave + 4 * j;
@@ -143,8 +152,8 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       }
     }
   };
-  auto dma_v = [&](int k0, bf16* vdst) {
-    const uint32_t base = (uint32_t)k0 * row_b;
+  auto dma_v = [&](int k0, bool need, bf16* vdst) {
+    const uint32_t base = need ? (uint32_t)k0 * row_b : kNoTile;
 #pragma unroll
     for (int j = 0; j < VSL / 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (GSA_LDS void*)&vdst[(wave + 4 * j) * 64 * 8], 16,
@@ -206,27 +215,29 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           o[dt] = mfma32x32x16(a, pb[sub][t], o[dt]);
         }
   };
-  // Online softmax of one Sᵀ tile: scale into the log2 domain, optional
-  // causal/length mask, row max (in-lane, then across the two wave halves),
-  // reference update, p = exp2(t - m), row sum folded into l, P packed to bf16.
-  // Returns whether any lane moved its reference (O must then be scaled by alpha).
+  // Online softmax of one Sᵀ tile in two halves (the reference test between
+  // them is the only branch of the loop body): row max in-lane, then across the
+  // two wave halves, and the reference update; then p = exp2(s·c − m), P
+  // packed to bf16 and the row sum folded into l.
   float alpha = 1.f;
-  auto softmax = [&](f32x16 (&s)[2], bool masked, int k0, bf16x8 (&pb)[2][2]) -> bool {
+  const bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
+  // causal / length mask of one Sᵀ tile: key offset within the tile of
+  // element (sub, r) is sub*32 + 8*(r/4) + 4*hl + r%4
+  auto apply_mask = [&](f32x16 (&s)[2], int k0) {
+    const int lim = min(my_q, S - 1) - k0 - 4 * hl;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sub][r] *= scale_log2;
-    if (masked) {
-      // key offset within the tile of element (sub, r): sub*32 + 8*(r/4) + 4*hl + r%4
-      const int lim = min(my_q, S - 1) - k0 - 4 * hl;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = sub * 32 + 8 * (r >> 2) + (r & 3);
-          s[sub][r] = off <= lim ? s[sub][r] : -INFINITY;
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int off = sub * 32 + 8 * (r >> 2) + (r & 3);
+        s[sub][r] = off <= lim ? s[sub][r] : -INFINITY;
+      }
+  };
+  // first half: row max, reference update; returns whether any lane moved
+  // its reference (O must then be scaled by alpha)
+  auto softmax_max = [&](f32x16 (&s)[2]) -> bool {
+    // row max of the raw scores (scaling by a positive constant and rounding
+    // are monotonic, so max(s)·c rounds to the max of the rounded s·c)
     float mx = s[0][0];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -239,26 +250,38 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     // move the reference only when the max grew by more than kRescale
     // (always on a row's first tile, where m_run = -inf)
-    const bool move = mx > m_run + kRescale;
-    const float m_new = move ? mx : m_run;
+    const float mx_t = mx * scale_log2;
+    const bool move = mx_t > m_run + kRescale;
+    const float m_new = move ? mx_t : m_run;
     alpha = fast_exp2(m_run - m_new);   // 1 when not moving, 0 on the first tile
     m_run = m_new;
-    float ps = 0.f;
+    return __any(move);
+  };
+  // second half: p = exp2(s·c − m), P packed to bf16, row sum folded into l
+  auto softmax_exp = [&](f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
+    const float neg_m = -m_run;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[sub][r] = fast_exp2(s[sub][r] - m_new);
-        ps += s[sub][r];
-      }
-    l_run = l_run * alpha + ps;
+      for (int r = 0; r < 16; ++r) s[sub][r] = fast_exp2(fmaf(s[sub][r], scale_log2, neg_m));
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[sub][t][e] = (bf16)s[sub][8 * t + e];
-    return __any(move);
+    // l sums the bf16-rounded p, the very weights the PV product applies
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2 pair = {pb[sub][t][2 * w], pb[sub][t][2 * w + 1]};
+          ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ps[w & 1], false);
+        }
+    l_run = l_run * alpha + (ps[0] + ps[1]);
   };
   auto rescale_o = [&]() {
 #pragma unroll
@@ -275,7 +298,10 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // (t+1)&1 holds K(t+1), V buffer t&1 holds V(t) and `cur` holds Sᵀ(t).  The
   // direct loads of K(t+2) and V(t+1) go to K buffer t&1 and V buffer (t+1)&1,
   // both last read in iteration t-1, and are waited for before the barrier.
-  // Sᵀ(t+1) runs on the matrix cores while the VALU works on softmax(t).
+  // The body is one basic block apart from the mask (diagonal tiles only, at
+  // the top) and the rare rescale, so the compiler interleaves the Sᵀ(t+1)
+  // matrix ops with the VALU work of softmax(t).  On the last tile Sᵀ(t+1)
+  // runs on whatever the K buffer holds and is discarded.
   // iteration `it` with compile-time buffer parity P = it & 1
   auto step = [&](auto parity, int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     constexpr int P = decltype(parity)::value;
@@ -284,21 +310,35 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     bf16* const v_cur = P ? Vs1 : Vs0;   // V(t)
     bf16* const v_nxt = P ? Vs0 : Vs1;   // refill with V(t+1)
     const int k0 = it * BN;
-    const bool has_next = it + 1 < n_kv;
-    if (it + 2 < n_kv) dma_k(k0 + 2 * BN, k_cur);
-    if (has_next) dma_v(k0 + BN, v_nxt);
-    if (has_next) mma_s(k_nxt, nxt);
-    const bool masked = (k0 + BN - 1 > qw0) || (k0 + BN > S);
+    if ((k0 + BN - 1 > qw0) || (k0 + BN > S)) apply_mask(cur, k0);
+    dma_k(k0 + 2 * BN, it + 2 < n_kv, k_cur);
+    dma_v(k0 + BN, it + 1 < n_kv, v_nxt);
+    mma_s(k_nxt, nxt);
+    const bool move = softmax_max(cur);
+    // the Sᵀ(t+1) block: LDS latency is several matrix ops long, so keep 8 K
+    // fragment reads in flight ahead of the matrix ops and fill their shadow
+    // with the row-max VALU work of softmax(t)
+    {
+      constexpr int NMF = 2 * D / 16;
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 8 < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+    }
+    if (move) rescale_o();
     bf16x8 pb[2][2];
-    if (softmax(cur, masked, k0, pb)) rescale_o();
+    softmax_exp(cur, pb);
     mma_pv(v_cur, pb);
     wait_dma_and_sync();
   };
 
   f32x16 sA[2], sB[2];
-  dma_k(0, Ks0);
-  dma_v(0, Vs0);
-  if (n_kv > 1) dma_k(BN, Ks1);
+  dma_k(0, true, Ks0);
+  dma_v(0, true, Vs0);
+  dma_k(BN, n_kv > 1, Ks1);
   wait_dma_and_sync();
   mma_s(Ks0, sA);
   __syncthreads();   // K buffer 0 is refilled in the first iteration

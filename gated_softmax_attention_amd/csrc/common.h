@@ -35,12 +35,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Hardware base-2 exponential (v_exp_f32): exp2(-inf) == 0, exp2(0) == 1 exactly.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Logistic sigmoid 1/(1+e^{-z}): hardware exp2, correctly rounded division.
-// z = 0 gives exactly 0.5; z >= 40 gives exactly 1.0 (e^{-z} is then below half
-// an ulp of 1); very negative z makes e^{-z} overflow to +inf and gives exactly 0.
+// Logistic sigmoid 1/(1+e^{-z}): hardware exp2 and hardware reciprocal (within
+// one ulp).  z = 0 gives exactly 0.5 and z >= 40 exactly 1.0 (e^{-z} is then
+// below half an ulp of 1; reciprocals of 2 and 1 are exact); very negative z
+// makes e^{-z} overflow to +inf and gives exactly 0.
 __device__ __forceinline__ float sigmoidf(float z) {
   float e = fast_exp2(-z * kLog2e);
-  return 1.0f / (1.0f + e);
+  return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {

@@ -169,6 +169,10 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
   using namespace gemm_big;
   __shared__ __align__(16) bf16 Xs[2][BM * XSL * 8];
   __shared__ __align__(16) bf16 Ws[2][BK * WSL * 8];
+  // landing area of the X load rounds that fall past the 36 instructions of a
+  // stage (waves 4..7 issue a fifth, out-of-range load so every wave runs the
+  // same branch-free code)
+  __shared__ __align__(16) bf16 Xpad[64 * 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,21 +211,24 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
     const int c = p ^ (4 * (row & 3));
     w_off[j] = (uint32_t)row * (uint32_t)N * 2 + (uint32_t)(n0 + 8 * c) * 2;
   }
+  // the load rounds of stage (k0, buf); a stage past the end of K (k0 >= K)
+  // loads nothing: every offset is out of range and the rounds write zeros
+  const uint32_t xpad = __builtin_amdgcn_readfirstlane(lds_addr(&Xpad[0]));
   auto dma = [&](int k0, int buf) {
     const uint32_t xd = __builtin_amdgcn_readfirstlane(lds_addr(&Xs[buf][0]));
     const uint32_t wd = __builtin_amdgcn_readfirstlane(lds_addr(&Ws[buf][0]));
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
       const int ins = wave + 8 * j;
-      if (ins < XINS) {
-        const uint32_t off = (k0 + x_kc[j] < K) ? x_off[j] + (uint32_t)k0 * 2 : kOOB;
-        dma16_lds(xr, off, xd + ins * 64 * 16);
-      }
+      const bool real = ins < XINS;
+      const uint32_t off = (real && k0 + x_kc[j] < K) ? x_off[j] + (uint32_t)k0 * 2 : kOOB;
+      dma16_lds(xr, off, real ? xd + ins * 64 * 16 : xpad);
     }
+    const bool live = k0 < K;
 #pragma unroll
     for (int j = 0; j < WINS / 8; ++j) {
       const int ins = wave + 8 * j;
-      dma16_lds(wr, w_off[j] + (uint32_t)k0 * (uint32_t)N * 2, wd + ins * 64 * 16);
+      dma16_lds(wr, live ? w_off[j] + (uint32_t)k0 * (uint32_t)N * 2 : kOOB, wd + ins * 64 * 16);
     }
   };
 
@@ -247,53 +254,83 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // one K step from the stage (xs, ws): 4 x 2 MFMA tiles, 4 k-steps of 16
-  auto compute = [&](const bf16* xs, const bf16* ws) {
-    GSA_LDS char* const wl = (GSA_LDS char*)(GSA_LDS void*)ws;
+  // MFMA operands of one 16-wide k step: 4 X fragments (A) and 2 W fragments (B)
+  struct Frag {
+    bf16x8 a[4], b[2];
+  };
+  auto load_frag = [&](int buf, int kk, Frag& f) {
+    const bf16* xs = &Xs[buf][0];
+    GSA_LDS char* const wl = (GSA_LDS char*)(GSA_LDS void*)&Ws[buf][0];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 a[4], b[2];
+    for (int mt = 0; mt < 4; ++mt) f.a[mt] = *(const bf16x8*)(xs + xa + (mt * 32 * XSL + 2 * kk) * 8);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = *(const bf16x8*)(xs + xa + (mt * 32 * XSL + 2 * kk) * 8);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        GSA_LDS char* const ad = wl + wb[nt] + 16 * kk * WSL * 16;
-        b[nt].lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)ad));
-        b[nt].hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(ad + 4 * WSL * 16)));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[mt], b[nt], acc[mt][nt]);
+    for (int nt = 0; nt < 2; ++nt) {
+      GSA_LDS char* const ad = wl + wb[nt] + 16 * kk * WSL * 16;
+      f.b[nt].lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)ad));
+      f.b[nt].hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(ad + 4 * WSL * 16)));
     }
   };
-  auto sync = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(f.a[mt], f.b[nt], acc[mt][nt]);
   };
 
+  // Pipeline: the fragments of k step kk+1 are read while the matrix ops of kk
+  // run.  Stage kt+1 is waited for (and every wave is past its reads of stage
+  // kt) at a barrier placed before the last k step of stage kt, so the reads of
+  // stage kt+1's first k step overlap that step's matrix ops; the direct loads
+  // of stage kt+2 then refill the buffer of stage kt.
   const int nk = (K + BK - 1) / BK;
+  static_assert(BK / 16 == 4, "four k steps per stage");
   dma(0, 0);
-  sync();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nk > 1) dma(BK, 1);
+  Frag f0, f1;
+  load_frag(0, 0, f0);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) dma((kt + 1) * BK, buf ^ 1);
-    compute(&Xs[buf][0], &Ws[buf][0]);
-    sync();
+    load_frag(buf, 1, f1);
+    mma(f0);
+    load_frag(buf, 2, f0);
+    mma(f1);
+    load_frag(buf, 3, f1);
+    mma(f0);
+    // each matrix op takes one of the next step's fragment reads along
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma((kt + 2) * BK, buf);          // past the end: out-of-range rounds
+    load_frag(buf ^ 1, 0, f0);        // on the last stage: stale, unused
+    mma(f1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
   }
 
+  // epilogue: lane holds column l32 of each 32x32 block, rows 8*(r/4) + 4*hl + r%4
+  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = n0 + wn * 64 + nt * 32 + l32;
+      const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (m < M && n < N) {
-          const float z = acc[mt][nt][r];
-          G[(int64_t)m * N + n] = apply_sigmoid ? sigmoidf(z) : z;
-        }
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        const float z = acc[mt][nt][r];
+        const float v = apply_sigmoid ? sigmoidf(z) : z;
+        if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
       }
     }
 }
