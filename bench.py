@@ -64,28 +64,34 @@ def measured_traffic(kernel_key, sources):
     return rec.get("bytes_per_launch")
 
 
-def time_steps(step, kernel, steps, warmup, torch):
-    """Run warmup + timed steps; events bracket the whole region and each launch
-    of the dominant kernel, all recorded on the current stream."""
+def time_steps(step, kernel_only, steps, warmup, torch):
+    """Warm up, then time exactly `steps` whole steps with events at the two ends
+    only (events between kernels add a dispatch gap of several microseconds).
+    Then time `steps` back-to-back launches of the dominant kernel alone, again
+    with one event pair, for its average launch duration.  All events are
+    recorded on the current stream, the one the library launches on."""
     for _ in range(warmup):
-        step(None)
-    torch.cuda.synchronize()
+        step()
     st = torch.cuda.current_stream()
-    k_start = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    k_end = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(st)
-    for i in range(steps):
-        step((k_start[i], k_end[i], st))
+    for _ in range(steps):
+        step()
     t_end.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    k_ms = sum(k_start[i].elapsed_time(k_end[i]) for i in range(steps)) / steps
-    return total_ms / steps, k_ms, wall
+    k_start = torch.cuda.Event(enable_timing=True)
+    k_end = torch.cuda.Event(enable_timing=True)
+    k_start.record(st)
+    for _ in range(steps):
+        kernel_only()
+    k_end.record(st)
+    torch.cuda.synchronize()
+    return total_ms / steps, k_start.elapsed_time(k_end) / steps, wall
 
 
 def prefill_bench(args, torch, gsa, cfg):
@@ -95,15 +101,14 @@ def prefill_bench(args, torch, gsa, cfg):
     G = torch.empty((cfg.B * cfg.S, cfg.N), dtype=torch.float32, device="cuda:0")
     Y = torch.empty_like(Q)
 
-    def step(ev):
+    def step():
         gsa.gate_logits(X, W, G=G)
-        if ev:
-            ev[0].record(ev[2])
         gsa.forward(Q, K, V, G, cfg.mode, Y=Y)
-        if ev:
-            ev[1].record(ev[2])
 
-    ms, fwd_ms, wall = time_steps(step, "attn", args.steps, args.warmup, torch)
+    def kernel_only():
+        gsa.forward(Q, K, V, G, cfg.mode, Y=Y)
+
+    ms, fwd_ms, wall = time_steps(step, kernel_only, args.steps, args.warmup, torch)
     if torch.isnan(Y[:, :64].float()).any():
         raise RuntimeError("NaN in output")
     flops = cfg.total_flops()
@@ -134,15 +139,14 @@ def decode_bench(args, torch, gsa, cfg):
     ws = torch.empty(gsa.decode_workspace_bytes(cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.D),
                      dtype=torch.uint8, device="cuda:0")
 
-    def step(ev):
+    def step():
         gsa.gate_logits(X, W, G=G)
-        if ev:
-            ev[0].record(ev[2])
         gsa.decode(Q, K, V, G, cfg.mode, Y=Y, workspace=ws)
-        if ev:
-            ev[1].record(ev[2])
 
-    ms, dec_ms, wall = time_steps(step, "decode", args.steps, args.warmup, torch)
+    def kernel_only():
+        gsa.decode(Q, K, V, G, cfg.mode, Y=Y, workspace=ws)
+
+    ms, dec_ms, wall = time_steps(step, kernel_only, args.steps, args.warmup, torch)
     if torch.isnan(Y.float()).any():
         raise RuntimeError("NaN in decode output")
     nbytes = cfg.decode_bytes()
