@@ -45,15 +45,20 @@ constexpr int BN = 64;   // keys per tile
 
 enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2 };
 
+#ifndef GSA_FWD_QB
+#define GSA_FWD_QB 1
+#endif
+
 #define GSA_LDS __attribute__((address_space(3)))
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 2)
+template <int D, int MODE, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1)
 void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                           const bf16* __restrict__ V, const float* __restrict__ Gate,
                           bf16* __restrict__ Y, int B, int S, int Hq, int Hkv, int n_qtiles,
                           float scale_log2) {
   using namespace fwd;
+  constexpr int BMQ = BM * QB;    // query rows per workgroup (QB blocks of 32 per wave)
   constexpr int CH = D / 8;       // 16-byte chunks per K/V row
   constexpr int KSL = CH + 1;     // K row stride in 16-B slots (one pad slot: 4-bank rotation per row)
   constexpr int VSL = CH;         // V rows are unpadded, chunk-swizzled
@@ -71,17 +76,31 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int l32 = lane & 31, hl = lane >> 5;
 
-  // heaviest (last) query tiles first, then heads, then batches
+  // Heaviest (last) query tiles first.  Workgroup ids are dealt round-robin
+  // over the 8 XCDs; when the (batch, head) pair count allows, XCD x = id % 8
+  // takes the x-th contiguous eighth of the pairs (pair = b*Hq + head, so the
+  // query heads of one GQA group are adjacent), which keeps a key/value head's
+  // tiles in one L2.
   const int bid = blockIdx.x;
   const int hb = Hq * B;
-  const int qt = n_qtiles - 1 - bid / hb;
-  const int head = (bid % hb) % Hq;
-  const int b = (bid % hb) / Hq;
+  int qt, pair;
+  if (hb % 8 == 0) {
+    const int pc = hb / 8, j = bid / 8;
+    qt = n_qtiles - 1 - j / pc;
+    pair = (bid % 8) * pc + j % pc;
+  } else {
+    qt = n_qtiles - 1 - bid / hb;
+    pair = bid % hb;
+  }
+  const int head = pair % Hq;
+  const int b = pair / Hq;
   const int kvh = head / (Hq / Hkv);
 
-  const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;  // first query row of this wave
-  const int my_q = qw0 + l32;      // this lane's query row
+  const int q0 = qt * BMQ;
+  const int qw0 = q0 + wave * 32 * QB;  // first query row of this wave
+  int my_q[QB];                         // this lane's query row in each 32-row block
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw0 + 32 * qb + l32;
 
   const int64_t q_row = (int64_t)Hq * D;
   const int64_t kv_row = (int64_t)Hkv * D;
@@ -91,27 +110,38 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 
   // Q fragments: B operand of Sᵀ = K·Qᵀ, lane holds Q[my_q][16*kk + 8*hl .. +7];
   // rows past the end read zeros (buffer range check) and are never stored
-  bf16x8 qf[D / 16];
+  bf16x8 qf[QB][D / 16];
   {
     const auto qr = make_rsrc(Qb, (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2));
-    const uint32_t qo = (uint32_t)(((int64_t)my_q * q_row + 8 * hl) * 2);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(qr, qo + 32 * kk, 0));
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t qo = (uint32_t)(((int64_t)my_q[qb] * q_row + 8 * hl) * 2);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[qb][kk] = __builtin_bit_cast(bf16x8, buffer_load16(qr, qo + 32 * kk, 0));
+    }
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[QB][D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][dt][r] = 0.f;
   // m_run is the reference max of the exp2-domain scores: it only moves when a
   // row's max grows by more than kRescale (then O and l are rescaled), so p may
   // reach 2^kRescale.  O/l does not depend on the reference (exact in real
   // arithmetic); a row's first tile always sets it.
   constexpr float kRescale = 8.0f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
-  const int kv_end = min(S, q0 + BM);
+  const int kv_end = min(S, q0 + BMQ);
   const int n_kv = ceil_div(kv_end, BN);
 
   // ---- global -> LDS: 16-byte direct loads (buffer_load ... lds); lane l of a
@@ -179,24 +209,28 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     vt_base[dt] = (uint32_t)(v_r * VSL * 16 + phys * 16 + (v_dc & 7) * 2);
   }
 
-  // Sᵀ tile (64 keys x this wave's 32 rows) from the K tile at ksrc; the two
-  // 32-key halves are independent accumulation chains, interleaved
-  auto mma_s = [&](const bf16* ksrc, f32x16 (&s)[2]) {
+  // Sᵀ tile (64 keys x this wave's 32·QB rows) from the K tile at ksrc; each K
+  // fragment serves the QB row blocks; the 2·QB accumulators are independent
+  // chains, interleaved
+  auto mma_s = [&](const bf16* ksrc, f32x16 (&s)[2][QB]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[sub][qb][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const bf16x8 a = *(const bf16x8*)(ksrc + ks_lane + (sub * 32 * KSL + 2 * kk) * 8);
-        s[sub] = mfma32x32x16(a, qf[kk], s[sub]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[sub][qb] = mfma32x32x16(a, qf[qb][kk], s[sub][qb]);
       }
   };
   // Oᵀ += Vᵀ·Pᵀ from the V tile at vsrc; the D/32 output blocks are
   // independent accumulation chains, interleaved
-  auto mma_pv = [&](const bf16* vsrc, const bf16x8 (&pb)[2][2]) {
+  auto mma_pv = [&](const bf16* vsrc, const bf16x8 (&pb)[QB][2][2]) {
     // an LDS pointer derived from the stage array (not from an integer), so
     // the compiler keeps the provenance it needs for its alias information
     GSA_LDS char* const vs = (GSA_LDS char*)(GSA_LDS void*)vsrc;
@@ -212,82 +246,98 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           bf16x8 a;
           a.lo = __builtin_bit_cast(bf16x4, lo);
           a.hi = __builtin_bit_cast(bf16x4, hi);
-          o[dt] = mfma32x32x16(a, pb[sub][t], o[dt]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma32x32x16(a, pb[qb][sub][t], o[qb][dt]);
         }
   };
   // Online softmax of one Sᵀ tile in two halves (the reference test between
   // them is the only branch of the loop body): row max in-lane, then across the
   // two wave halves, and the reference update; then p = exp2(s·c − m), P
   // packed to bf16 and the row sum folded into l.
-  float alpha = 1.f;
+  float alpha[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f;
   const bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
   // causal / length mask of one Sᵀ tile: key offset within the tile of
   // element (sub, r) is sub*32 + 8*(r/4) + 4*hl + r%4
-  auto apply_mask = [&](f32x16 (&s)[2], int k0) {
-    const int lim = min(my_q, S - 1) - k0 - 4 * hl;
+  auto apply_mask = [&](f32x16 (&s)[2][QB], int k0) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int lim = min(my_q[qb], S - 1) - k0 - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = sub * 32 + 8 * (r >> 2) + (r & 3);
-        s[sub][r] = off <= lim ? s[sub][r] : -INFINITY;
-      }
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = sub * 32 + 8 * (r >> 2) + (r & 3);
+          s[sub][qb][r] = off <= lim ? s[sub][qb][r] : -INFINITY;
+        }
+    }
   };
   // first half: row max, reference update; returns whether any lane moved
   // its reference (O must then be scaled by alpha)
-  auto softmax_max = [&](f32x16 (&s)[2]) -> bool {
-    // row max of the raw scores (scaling by a positive constant and rounding
-    // are monotonic, so max(s)·c rounds to the max of the rounded s·c)
-    float mx = s[0][0];
+  auto softmax_max = [&](f32x16 (&s)[2][QB]) -> bool {
+    bool moved = false;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int qb = 0; qb < QB; ++qb) {
+      // row max of the raw scores (scaling by a positive constant and rounding
+      // are monotonic, so max(s)·c rounds to the max of the rounded s·c)
+      float mx = s[0][qb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    {
-      // max with the other wave half (same query row, the other 32 keys)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][qb][r]);
+      {
+        // max with the other wave half (same query row, the other 32 keys)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+      }
+      // move the reference only when the max grew by more than kRescale
+      // (always on a row's first tile, where m_run = -inf)
+      const float mx_t = mx * scale_log2;
+      const bool move = mx_t > m_run[qb] + kRescale;
+      const float m_new = move ? mx_t : m_run[qb];
+      alpha[qb] = fast_exp2(m_run[qb] - m_new);   // 1 when not moving, 0 on the first tile
+      m_run[qb] = m_new;
+      moved = moved || move;
     }
-    // move the reference only when the max grew by more than kRescale
-    // (always on a row's first tile, where m_run = -inf)
-    const float mx_t = mx * scale_log2;
-    const bool move = mx_t > m_run + kRescale;
-    const float m_new = move ? mx_t : m_run;
-    alpha = fast_exp2(m_run - m_new);   // 1 when not moving, 0 on the first tile
-    m_run = m_new;
-    return __any(move);
+    return __any(moved);
   };
   // second half: p = exp2(s·c − m), P packed to bf16, row sum folded into l
-  auto softmax_exp = [&](f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
-    const float neg_m = -m_run;
+  auto softmax_exp = [&](f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2]) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = -m_run[qb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sub][r] = fast_exp2(fmaf(s[sub][r], scale_log2, neg_m));
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+        for (int r = 0; r < 16; ++r) s[sub][qb][r] = fast_exp2(fmaf(s[sub][qb][r], scale_log2, neg_m));
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[sub][t][e] = (bf16)s[sub][8 * t + e];
-    // l sums the bf16-rounded p, the very weights the PV product applies
-    float ps[2] = {0.f, 0.f};
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+          for (int e = 0; e < 8; ++e) pb[qb][sub][t][e] = (bf16)s[sub][qb][8 * t + e];
+      // l sums the bf16-rounded p, the very weights the PV product applies
+      float ps[2] = {0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const bf16x2 pair = {pb[sub][t][2 * w], pb[sub][t][2 * w + 1]};
-          ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ps[w & 1], false);
-        }
-    l_run = l_run * alpha + (ps[0] + ps[1]);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const bf16x2 pair = {pb[qb][sub][t][2 * w], pb[qb][sub][t][2 * w + 1]};
+            ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ps[w & 1], false);
+          }
+      l_run[qb] = l_run[qb] * alpha[qb] + (ps[0] + ps[1]);
+    }
   };
   auto rescale_o = [&]() {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][dt][r] *= alpha[qb];
   };
   auto wait_dma_and_sync = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -303,7 +353,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // matrix ops with the VALU work of softmax(t).  On the last tile Sᵀ(t+1)
   // runs on whatever the K buffer holds and is discarded.
   // iteration `it` with compile-time buffer parity P = it & 1
-  auto step = [&](auto parity, int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  auto step = [&](auto parity, int it, f32x16 (&cur)[2][QB], f32x16 (&nxt)[2][QB]) {
     constexpr int P = decltype(parity)::value;
     bf16* const k_cur = P ? Ks1 : Ks0;   // held K(t), consumed in iteration t-1: refill with K(t+2)
     bf16* const k_nxt = P ? Ks0 : Ks1;   // K(t+1)
@@ -319,23 +369,23 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     // fragment reads in flight ahead of the matrix ops and fill their shadow
     // with the row-max VALU work of softmax(t)
     {
-      constexpr int NMF = 2 * D / 16;
+      constexpr int NRD = 2 * D / 16;   // K fragment reads, each feeding QB matrix ops
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < NMF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + 8 < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      for (int i = 0; i < NRD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        if (i + 8 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * QB, 0);
       }
     }
     if (move) rescale_o();
-    bf16x8 pb[2][2];
+    bf16x8 pb[QB][2][2];
     softmax_exp(cur, pb);
     mma_pv(v_cur, pb);
     wait_dma_and_sync();
   };
 
-  f32x16 sA[2], sB[2];
+  f32x16 sA[2][QB], sB[2][QB];
   dma_k(0, true, Ks0);
   dma_v(0, true, Vs0);
   dma_k(BN, n_kv > 1, Ks1);
@@ -347,31 +397,35 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if (it + 1 < n_kv) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
   }
 
-  if (my_q >= S) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);  // the two halves summed different keys
-  const float inv = 1.0f / l_tot;
-  const int64_t tok = (int64_t)b * S + my_q;
-  bf16* yrow = Y + tok * q_row + (int64_t)head * D;
-  float gh = 1.0f;
-  if constexpr (MODE == kGateHead) gh = Gate[tok * Hq + head];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int qb = 0; qb < QB; ++qb) {
+    // every lane takes part in the exchange; rows past the end store nothing
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);  // the two halves summed different keys
+    if (my_q[qb] >= S) continue;
+    const float inv = 1.0f / l_tot;
+    const int64_t tok = (int64_t)b * S + my_q[qb];
+    bf16* yrow = Y + tok * q_row + (int64_t)head * D;
+    float gh = 1.0f;
+    if constexpr (MODE == kGateHead) gh = Gate[tok * Hq + head];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = dt * 32 + 8 * i + 4 * hl;
-      float y[4];
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = o[dt][4 * i + j] * inv;
-      if constexpr (MODE == kGateElem) {
-        const f32x4 g = *(const f32x4*)(Gate + tok * q_row + (int64_t)head * D + d0);
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = dt * 32 + 8 * i + 4 * hl;
+        float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] *= g[j];
-      } else if constexpr (MODE == kGateHead) {
+        for (int j = 0; j < 4; ++j) y[j] = o[qb][dt][4 * i + j] * inv;
+        if constexpr (MODE == kGateElem) {
+          const f32x4 g = *(const f32x4*)(Gate + tok * q_row + (int64_t)head * D + d0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] *= gh;
+          for (int j = 0; j < 4; ++j) y[j] *= g[j];
+        } else if constexpr (MODE == kGateHead) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] *= gh;
+        }
+        *(u32x2*)(yrow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
       }
-      *(u32x2*)(yrow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    }
+  }
 }
 
 // float32 kernel, also used for decode in float32: S query rows aligned to the
@@ -461,12 +515,12 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int QB = GSA_FWD_QB>
 static void launch_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
                         int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st) {
-  const int nq = ceil_div(S, fwd::BM);
+  const int nq = ceil_div(S, fwd::BM * QB);
   const int64_t blocks = (int64_t)nq * Hq * B;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE>), dim3((unsigned)blocks), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE, QB>), dim3((unsigned)blocks), dim3(256), 0, st,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, B, S, Hq, Hkv,
                      nq, scale_log2);
 }
