@@ -152,9 +152,7 @@ void gate_gemm_bf16_kernel(const bf16* __restrict__ X, const bf16* __restrict__ 
 //           transposed reads (ds_read_b64_tr_b16), 4 k values each.
 // Workgroups are mapped so that each XCD (workgroup id mod 8) owns a
 // contiguous range of M tiles: an X row block is fetched into one L2 only.
-// The k order of every output's sum (16-wide MFMA steps, increasing k, one
-// accumulator) is the same as in the narrow kernel below, so both produce
-// bitwise identical scores.
+// Every output is one accumulator over 16-wide MFMA steps in increasing k.
 namespace gemm_big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int XSL = BK / 8 + 1;   // 9 slots per X row
@@ -336,33 +334,42 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
 }
 
 // Narrow / short bf16 gate projection for shapes with few rows (decode: one
-// token per batch) or few columns (headwise gate: one per head): each
-// single-wave workgroup owns one 32×32 output tile and streams the whole K
-// through an 8-stage ring of LDS buffers filled by 16-byte direct loads, so up
-// to 7 stages (56 KB) are in flight per wave.  No barrier is needed: a wave
-// only reads what its own loads wrote, after waiting on them.
+// token per batch) or few columns (headwise gate: one per head).  Each
+// 4-wave workgroup owns one 32×32 output tile; wave w sums the w-th quarter of
+// K, streaming it through its own 4-stage ring of LDS buffers filled by
+// 16-byte direct loads (3 stages, 24 KB, in flight per wave).  No barrier is
+// needed inside the ring: a wave only reads what its own loads wrote, after
+// waiting on them.  At the end the four partial sums are added through LDS in
+// wave order and wave 0 applies σ and stores.
 //   X stage: 32 rows × 8 chunks (k 64), chunk index XOR (row & 7); the A
 //            operand is one 16-B read.
 //   W stage: 64 rows (k) × 4 chunks (32 columns, 64 B), unswizzled (eight
 //            consecutive rows are 512 contiguous bytes); the B operand comes
 //            from two transposed reads.
 namespace gemm_narrow {
-constexpr int BK = 64, NS = 8;
+constexpr int BK = 64, NS = 4, WAVES = 4;
 constexpr int XSLOTS = 32 * 8, WSLOTS = 64 * 4;     // 16-B slots per stage
 constexpr uint32_t kOOB = 0xfffffff0u;
 }  // namespace gemm_narrow
 
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(256)
 void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                                   float* __restrict__ G, int M, int K, int N, int tiles_n,
                                   int apply_sigmoid) {
   using namespace gemm_narrow;
-  __shared__ __align__(16) bf16 Xs[NS][XSLOTS * 8];
-  __shared__ __align__(16) bf16 Ws[NS][WSLOTS * 8];
-  const int lane = threadIdx.x;
+  __shared__ __align__(16) bf16 Xs[WAVES][NS][XSLOTS * 8];
+  __shared__ __align__(16) bf16 Ws[WAVES][NS][WSLOTS * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int m0 = tm * 32, n0 = tn * 32;
+
+  // this wave's k range: a whole number of BK steps
+  const int nk_all = (K + BK - 1) / BK;
+  const int nk_w = (nk_all + WAVES - 1) / WAVES;
+  const int kt0 = wave * nk_w;
+  const int nk = max(0, min(nk_all, kt0 + nk_w) - kt0);
 
   const auto xr = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
   const auto wr = make_rsrc(W, (uint32_t)((int64_t)K * N * 2));
@@ -382,8 +389,8 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
   }
   const bool n_ok = (N % 8) == 0;
   auto dma = [&](int k0, int st) {
-    const uint32_t xd = __builtin_amdgcn_readfirstlane(lds_addr(&Xs[st][0]));
-    const uint32_t wd = __builtin_amdgcn_readfirstlane(lds_addr(&Ws[st][0]));
+    const uint32_t xd = __builtin_amdgcn_readfirstlane(lds_addr(&Xs[wave][st][0]));
+    const uint32_t wd = __builtin_amdgcn_readfirstlane(lds_addr(&Ws[wave][st][0]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (k0 + x_k[i] < K) ? x_off[i] + (uint32_t)k0 * 2 : kOOB;
@@ -397,8 +404,8 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
   };
 
   // A operand: row l32, chunk 2*kk + hl, stored at chunk ^ (l32 & 7)
-  const uint32_t xs0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Xs[0][0];
-  const uint32_t ws0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Ws[0][0];
+  const uint32_t xs0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Xs[wave][0][0];
+  const uint32_t ws0 = (uint32_t)(uintptr_t)(GSA_LDS void*)&Ws[wave][0][0];
   // B operand: supplier lane (g, si) names k row 8*(g/2) + si/4 (+4a +16kk) and
   // columns 16*(g%2) + 4*(si%4) .. +3 of the 32-column stage
   const int g = lane >> 4, si = lane & 15;
@@ -407,16 +414,15 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int nk = (K + BK - 1) / BK;
-  // prologue: stages 0 .. NS-2 in flight
+  // prologue: stages 0 .. NS-2 of this wave's range in flight
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) dma(st * BK, st);
+    if (st < nk) dma((kt0 + st) * BK, st);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % NS;
     if (kt + NS - 1 < nk) {
-      dma((kt + NS - 1) * BK, (kt + NS - 1) % NS);
-      asm volatile("s_waitcnt vmcnt(56)" ::: "memory");   // the 7 newer stages (8 loads each) may still fly
+      dma((kt0 + kt + NS - 1) * BK, (kt + NS - 1) % NS);
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // the 3 newer stages (8 loads each) may still fly
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -432,6 +438,21 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
       acc = mfma32x32x16(a, b, acc);
     }
   }
+
+  // add the four partial sums in wave order through LDS (the X ring of waves
+  // 1..3 is reused once every wave is past its last read)
+  __syncthreads();
+  float* const red = (float*)&Xs[0][0][0];   // [3][16][64] floats = 12 KB
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += red[(w * 16 + r) * 64 + lane];
   const int n = n0 + l32;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -498,7 +519,7 @@ hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, i
   } else if (bf16_inputs && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) && K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, 32);
     const int64_t tiles = ceil_div<int64_t>(M, 32) * tiles_n;
-    hipLaunchKernelGGL(gate_gemm_bf16_narrow_kernel, dim3((unsigned)tiles), dim3(64), 0, stream,
+    hipLaunchKernelGGL(gate_gemm_bf16_narrow_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_n,
                        (int)apply_sigmoid);
   } else if (bf16_inputs) {
