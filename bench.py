@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--only", choices=["prefill", "decode"], default=None,
                    help="run one workload's GPU part only (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the gqa_prefill and long_prefill lines (reported beside the headline)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run only a plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
@@ -114,13 +116,13 @@ def prefill_bench(args, torch, gsa, cfg):
     flops = cfg.total_flops()
     fwd_flops = cfg.attention_flops()
     achieved = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    traffic = measured_traffic("attn_fwd_dense_prefill", ["attn_fwd.hip", "common.h"])
+    traffic = measured_traffic(f"attn_fwd_{cfg.name}", ["attn_fwd.hip", "common.h"])
     return {
         "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "wall_s": wall,
         "roofline": {
-            "kernel": "attn_fwd_bf16_kernel<128, elementwise>",
+            "kernel": f"attn_fwd_bf16_kernel<{cfg.D}, {cfg.mode}>",
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
             "avg_launch_ms": fwd_ms, "algorithmic_flops_per_launch": fwd_flops,
@@ -265,6 +267,25 @@ def main():
                    "roofline": dec["roofline"]}
         else:
             out["decode"] = dec
+    if out is not None and not args.no_others and args.only is None:
+        # the other prefill workloads, each its own gate GEMM + forward step
+        others = {}
+        for name in ("gqa_prefill", "long_prefill"):
+            cfg = CONFIGS[name]
+            r = prefill_bench(args, torch, gsa, cfg)
+            torch.cuda.empty_cache()
+            print(f"# {name}: {r['ms_per_step']:.4f} ms/step, {r['tflops']:.1f} TFLOP/s; forward "
+                  f"{r['roofline']['avg_launch_ms']:.4f} ms = {r['roofline']['achieved']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            others[name] = {
+                "value": r["tflops"], "unit": "TFLOP/s", "ms_per_step": r["ms_per_step"],
+                "pct_of_peak": 100.0 * r["tflops"] / PEAK_BF16_TFLOPS,
+                "config": {"B": cfg.B, "S": cfg.S, "d_model": cfg.d_model, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                           "D": cfg.D, "mode": cfg.mode, "causal": True,
+                           "flops_per_step": cfg.total_flops()},
+                "roofline": r["roofline"], "gate_ms_per_step": r["gate_ms_per_step"],
+            }
+        out["other_prefill"] = others
     if out is not None and not args.no_cpu_baseline and args.only is None:
         print("# timing the oracle on the host ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args, torch, pcfg)

@@ -285,7 +285,10 @@ void decode_merge_bf16_kernel(const float* __restrict__ part, const float* __res
 int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv) {
   const int64_t G = Hq / Hkv;
   const int64_t base = B * Hkv * ((G + 3) / 4);
-  int64_t ns = (2048 + base - 1) / base;           // aim for >= 2048 workgroups
+  // aim for >= 1024 workgroups: one fits a CU (its LDS ring), so that is about
+  // four dispatch rounds on 256 CUs; more splits add rounds and partials
+  // without adding bytes in flight
+  int64_t ns = (1024 + base - 1) / base;
   const int64_t max_ns = (L + 255) / 256;          // but at least 256 keys per split
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
