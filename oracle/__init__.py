@@ -17,15 +17,20 @@ Sources (page titles; sections):
     before concat) and the GatedAttentionOutput snippet (bias-free projection,
     view of the gate as [B, T, n_h, d_h] or [B, T, n_h, 1]).
 
-Every function here is pinned by tests in ``tests/test_oracle.py`` (brute-force
-loops, a library SDPA in float64, closed forms and invariants); none is
-"parity unpinned".
+Every function here is pinned by tests in ``tests/test_oracle.py`` and
+``tests/test_oracle_backward.py`` (brute-force loops, central differences of the
+brute-force forward, a library SDPA and a library autodiff in float64, closed
+forms and invariants); none is "parity unpinned".
+
+The backward (``backward.py``) is the chain rule on the plain forward; its gate
+branch follows the "Gated Attention如何用1%的参数量…" page, §2.2 gradient analysis.
 """
 from .gated_sdpa import (
     gate_scores, sigmoid, gate_values, sdpa, gated_sdpa, gated_decode,
     gate_param_count,
 )
+from .backward import sdpa_backward, gated_sdpa_backward
 from . import brute
 
 __all__ = ["gate_scores", "sigmoid", "gate_values", "sdpa", "gated_sdpa", "gated_decode",
-           "gate_param_count", "brute"]
+           "gate_param_count", "sdpa_backward", "gated_sdpa_backward", "brute"]

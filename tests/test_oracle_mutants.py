@@ -73,3 +73,75 @@ def test_unmutated_copy_passes():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     assert not pins_pass(load_mutant(name))
+
+
+# ---------------------------------------------------------------- backward oracle
+BWD_SRC = os.path.join(os.path.dirname(SRC), "backward.py")
+
+BWD_MUTANTS = {
+    "sigmoid_derivative_dropped": ("dZ = dg * g * (1.0 - g)", "dZ = dg * g"),
+    "softmax_row_term_dropped": ("dS = P * (dP - (dP * P).sum(axis=-1, keepdims=True))", "dS = P * dP"),
+    "dk_unscaled": ("dK[b, :, c, :] += (dS.T @ q) * scale", "dK[b, :, c, :] += dS.T @ q"),
+    "dq_uses_values": ("dQ[b, :, h, :] = (dS @ Kc) * scale", "dQ[b, :, h, :] = (dS @ Vc) * scale"),
+    "dv_untransposed_probs": ("dV[b, :, c, :] += P.T @ dy", "dV[b, :, c, :] += P @ dy"),
+    "upstream_not_gated": ("dY = dYg * gv ", "dY = dYg "),
+    "gate_grad_uses_gated_output": ("dgv = dYg * Y ", "dgv = dYg * Y * gv "),
+    "headwise_mean_not_sum": ("dg = dgv.sum(axis=-1)", "dg = dgv.mean(axis=-1)"),
+    "gqa_interleaved": ("c = h // G", "c = h % Hkv"),
+    "dw_not_summed_over_batch": ("dW = X.reshape(B * S, -1).T @ dZ.reshape(B * S, -1)", "dW = X[0].T @ dZ[0]"),
+    "bwd_mask_excludes_self": ("<= (np.arange(S) + off)[:, None]", "< (np.arange(S) + off)[:, None]"),
+}
+
+
+def load_bwd_mutant(name):
+    with open(BWD_SRC) as f:
+        src = f.read().replace("from .gated_sdpa import", "from oracle.gated_sdpa import")
+    if name is not None:
+        old, new = BWD_MUTANTS[name]
+        assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_bwd_mutant_{name}")
+    exec(compile(src, f"<bwd mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def bwd_pins_pass(orc):
+    """Central differences of the brute-force forward on tiny shapes, every mode."""
+    rng = np.random.default_rng(17)
+    h = 1e-5
+    try:
+        for (B, S, Hq, Hkv, D, dm, mode) in [(2, 3, 4, 2, 2, 3, "elementwise"),
+                                             (2, 3, 4, 2, 2, 3, "headwise")]:
+            N = Hq * D if mode == "elementwise" else Hq
+            t = dict(X=rng.standard_normal((B, S, dm)), W=rng.standard_normal((dm, N)),
+                     Q=rng.standard_normal((B, S, Hq, D)), K=rng.standard_normal((B, S, Hkv, D)),
+                     V=rng.standard_normal((B, S, Hkv, D)))
+            dYg = rng.standard_normal((B, S, Hq, D))
+            got = orc.gated_sdpa_backward(t["X"], t["W"], t["Q"], t["K"], t["V"], dYg, mode)
+
+            def loss():
+                Yg = np.array(brute.gated_sdpa(t["X"], t["W"], t["Q"], t["K"], t["V"], mode))
+                return math.fsum((Yg * dYg).ravel())
+            for name in ("Q", "K", "V", "X", "W"):
+                arr = t[name]
+                for idx in np.ndindex(arr.shape):
+                    keep = arr[idx]
+                    arr[idx] = keep + h
+                    lp = loss()
+                    arr[idx] = keep - h
+                    lm = loss()
+                    arr[idx] = keep
+                    if not abs((lp - lm) / (2 * h) - got["d" + name][idx]) <= 1e-6:
+                        return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unmutated_backward_copy_passes():
+    assert bwd_pins_pass(load_bwd_mutant(None))
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    assert not bwd_pins_pass(load_bwd_mutant(name))
