@@ -6,10 +6,12 @@ properties, allocates outputs with torch and passes device pointers and the
 current HIP stream.  There is no CPU or PyTorch fallback: calls fail loudly
 when the library is missing or no GPU is present.
 """
-from .ops import (gate_logits, forward, decode, gated_attention, gated_decode,
-                  decode_workspace_bytes, decode_num_splits, MODES)
+from .ops import (gate_logits, forward, forward_lse, decode, gated_attention, gated_decode,
+                  decode_workspace_bytes, decode_num_splits, backward, backward_workspace_bytes,
+                  MODES)
 from ._lib import GsaError, load as load_library, LIB_PATH
 
-__all__ = ["gate_logits", "forward", "decode", "gated_attention", "gated_decode",
-           "decode_workspace_bytes", "decode_num_splits", "MODES", "GsaError",
+__all__ = ["gate_logits", "forward", "forward_lse", "decode", "gated_attention", "gated_decode",
+           "decode_workspace_bytes", "decode_num_splits", "backward",
+           "backward_workspace_bytes", "MODES", "GsaError",
            "load_library", "LIB_PATH"]

@@ -28,9 +28,12 @@ SIGNATURES = {
     "gsa_last_error_message": (ctypes.c_char_p, []),
     "gsa_gate_logits": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _P]),
+    "gsa_forward_lse": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_decode_num_splits": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
     "gsa_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I]),
     "gsa_decode": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
+    "gsa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64, _I]),
+    "gsa_backward": (_I, [_P] * 14 + [_I64] * 6 + [_I, _I, _P, _SZ, _P]),
 }
 
 _lib = None

@@ -15,13 +15,22 @@ namespace gsa {
 hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, int64_t K, int64_t N,
                             bool bf16_inputs, bool apply_sigmoid, hipStream_t stream);
 hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const float* G, void* Y,
-                           int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
+                           float* Lse, int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
                            bool bf16_inputs, hipStream_t stream);
 hipError_t launch_decode_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
                               void* workspace, int B, int L, int Hq, int Hkv, int D, int mode,
                               int nsplit, hipStream_t stream);
 int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv);
 int64_t decode_chunk(int64_t L, int64_t nsplit);
+hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
+                           const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
+                           float* Dv, void* dZ, int B, int S, int Hq, int Hkv, int D, int mode,
+                           hipStream_t stream);
+hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
+                              int64_t N, hipStream_t st);
+hipError_t launch_bwd_gemm_dw(const void* X, const void* dZ, float* dW, float* partials, int64_t M,
+                              int64_t d_model, int64_t N, int64_t splits, hipStream_t st);
+int64_t bwd_dw_splits(int64_t M, int64_t d_model, int64_t N);
 }  // namespace gsa
 
 namespace {
@@ -157,18 +166,35 @@ gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, in
                     "gsa_gate_logits launch");
 }
 
+namespace {
+gsa_status forward_impl(const char* fn, const void* Q, const void* K, const void* V, const float* G,
+                        void* Y, float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                        int64_t D, int mode, int dtype, void* stream) {
+  if (!Q || !K || !V || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (gsa_status st = check_attn_shape(fn, B, S, Hq, Hkv, D, mode, G)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "%s: Q, K, V, G and Y must be 16-byte aligned", fn);
+  if (LSE && ((uintptr_t)LSE % 4) != 0)
+    return fail(GSA_ERR_MISALIGNED, "%s: LSE must be 4-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_attn_fwd(Q, K, V, G, Y, LSE, (int)B, (int)S, (int)S, (int)Hq, (int)Hkv,
+                                         (int)D, mode, dtype == GSA_BF16, (hipStream_t)stream),
+                    fn);
+}
+}  // namespace
+
 gsa_status gsa_forward(const void* Q, const void* K, const void* V, const float* G, void* Y,
                        int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype,
                        void* stream) {
-  if (!Q || !K || !V || !Y) return fail(GSA_ERR_INVALID_ARG, "gsa_forward: null pointer");
-  if (gsa_status st = check_attn_shape("gsa_forward", B, S, Hq, Hkv, D, mode, G)) return st;
-  if (gsa_status st = check_dtype("gsa_forward", dtype)) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || (G && !aligned16(G)))
-    return fail(GSA_ERR_MISALIGNED, "gsa_forward: Q, K, V, G and Y must be 16-byte aligned");
-  if (gsa_status st = check_device()) return st;
-  return hip_result(gsa::launch_attn_fwd(Q, K, V, G, Y, (int)B, (int)S, (int)S, (int)Hq, (int)Hkv, (int)D,
-                                         mode, dtype == GSA_BF16, (hipStream_t)stream),
-                    "gsa_forward launch");
+  return forward_impl("gsa_forward", Q, K, V, G, Y, nullptr, B, S, Hq, Hkv, D, mode, dtype, stream);
+}
+
+gsa_status gsa_forward_lse(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                           float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                           int mode, int dtype, void* stream) {
+  if (!LSE) return fail(GSA_ERR_INVALID_ARG, "gsa_forward_lse: null pointer");
+  return forward_impl("gsa_forward_lse", Q, K, V, G, Y, LSE, B, S, Hq, Hkv, D, mode, dtype, stream);
 }
 
 int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int num_splits) {
@@ -214,9 +240,101 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
                                               (int)Hkv, (int)D, mode, (int)ns, (hipStream_t)stream),
                       "gsa_decode launch");
   // float32: the general kernel with one query row aligned to the end of the cache
-  return hip_result(gsa::launch_attn_fwd(Q, Kc, Vc, G, Y, (int)B, 1, (int)L, (int)Hq, (int)Hkv, (int)D,
+  return hip_result(gsa::launch_attn_fwd(Q, Kc, Vc, G, Y, nullptr, (int)B, 1, (int)L, (int)Hq, (int)Hkv, (int)D,
                                          mode, false, (hipStream_t)stream),
                     "gsa_decode launch");
+}
+
+namespace {
+// Workspace of gsa_backward, each region 256-byte aligned:
+//   dY  = dY' ⊙ g      bf16 [B, S, Hq, D]   (gated modes)
+//   Dv  = Σ_d dY'·Y'   fp32 [B, Hq, S]
+//   dZ                 bf16 [B*S, N]        (gated modes)
+//   dW_θ partials      fp32 [splits, d_model, N]  (gated modes, splits > 1)
+struct BwdLayout {
+  size_t dy = 0, dv = 0, dz = 0, part = 0, total = 0;
+  int64_t splits = 1;
+};
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdLayout bwd_layout(int64_t B, int64_t S, int64_t Hq, int64_t D, int64_t d_model, int mode) {
+  BwdLayout l;
+  const bool gated = mode != GSA_GATE_NONE;
+  const int64_t M = B * S, N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
+  size_t off = 0;
+  l.dy = off;
+  if (gated) off += align256((size_t)(M * Hq * D) * 2);
+  l.dv = off;
+  off += align256((size_t)(B * Hq * S) * 4);
+  l.dz = off;
+  if (gated) off += align256((size_t)(M * N) * 2);
+  l.part = off;
+  if (gated) {
+    l.splits = gsa::bwd_dw_splits(M, d_model, N);
+    if (l.splits > 1) off += align256((size_t)(l.splits * d_model * N) * 4);
+  }
+  l.total = off;
+  return l;
+}
+constexpr int64_t kU32Bytes = 0xfffffff0LL;   // operands addressed with 32-bit byte offsets
+}  // namespace
+
+size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t d_model, int mode) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
+  if (mode != GSA_GATE_NONE && mode != GSA_GATE_ELEMENTWISE && mode != GSA_GATE_HEADWISE) return 0;
+  if (mode != GSA_GATE_NONE && d_model <= 0) return 0;
+  if (B * S > kIntMax || Hq > 4096 || D > 128 || d_model > kIntMax) return 0;
+  return bwd_layout(B, S, Hq, D, d_model, mode).total;
+}
+
+gsa_status gsa_backward(const void* X, const void* W, const float* G, const void* Q, const void* K,
+                        const void* V, const void* Y, const float* LSE, const void* dY, void* dX,
+                        float* dW, void* dQ, void* dK, void* dV, int64_t B, int64_t S, int64_t Hq,
+                        int64_t Hkv, int64_t D, int64_t d_model, int mode, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* fn = "gsa_backward";
+  if (!Q || !K || !V || !Y || !LSE || !dY || !dQ || !dK || !dV)
+    return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (gsa_status st = check_attn_shape(fn, B, S, Hq, Hkv, D, mode, G)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "%s: only GSA_BF16 is supported", fn);
+  const bool gated = mode != GSA_GATE_NONE;
+  if (gated != (X != nullptr) || gated != (W != nullptr) || gated != (dX != nullptr) || gated != (dW != nullptr))
+    return fail(GSA_ERR_INVALID_ARG, "%s: X, W, dX and dW must be given exactly when a gate is", fn);
+  const int64_t M = B * S, N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
+  if (gated) {
+    if (d_model <= 0 || d_model > kIntMax)
+      return fail(GSA_ERR_INVALID_ARG, "%s: d_model=%lld must be positive", fn, (long long)d_model);
+    if (d_model % 8 != 0 || N % 8 != 0)
+      return fail(GSA_ERR_UNSUPPORTED, "%s: d_model=%lld and the gate width %lld must be multiples of 8", fn,
+                  (long long)d_model, (long long)N);
+    if (M * d_model * 2 > kU32Bytes || M * N * 2 > kU32Bytes || d_model * N * 4 > kU32Bytes)
+      return fail(GSA_ERR_UNSUPPORTED, "%s: X, dZ or W_theta exceeds 4 GiB", fn);
+  }
+  const void* ptrs[] = {X, W, G, Q, K, V, Y, dY, dX, dW, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p))
+      return fail(GSA_ERR_MISALIGNED, "%s: every tensor and the workspace must be 16-byte aligned", fn);
+  if (((uintptr_t)LSE % 4) != 0) return fail(GSA_ERR_MISALIGNED, "%s: LSE must be 4-byte aligned", fn);
+  const BwdLayout lay = bwd_layout(B, S, Hq, D, d_model, mode);
+  if (workspace == nullptr || workspace_bytes < lay.total)
+    return fail(GSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (gsa_status st = check_device()) return st;
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  void* dz = gated ? ws + lay.dz : nullptr;
+  hipError_t e = gsa::launch_attn_bwd(Q, K, V, dY, Y, G, LSE, dQ, dK, dV, gated ? ws + lay.dy : nullptr,
+                                      (float*)(ws + lay.dv), dz, (int)B, (int)S, (int)Hq, (int)Hkv, (int)D,
+                                      mode, st);
+  if (e != hipSuccess) return hip_result(e, "gsa_backward attention launch");
+  if (gated) {
+    e = gsa::launch_bwd_gemm_dx(dz, W, dX, M, d_model, N, st);
+    if (e != hipSuccess) return hip_result(e, "gsa_backward dX launch");
+    e = gsa::launch_bwd_gemm_dw(X, dz, dW, (float*)(ws + lay.part), M, d_model, N, lay.splits, st);
+    if (e != hipSuccess) return hip_result(e, "gsa_backward dW launch");
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -1,0 +1,526 @@
+// Backward of causal gated SDPA (bf16, D in {64, 128}).
+//
+// The gradients are the chain rule on the forward (see the "Gated Attention如何
+// 用1%的参数量…" page, §2.2 gradient analysis, for the gate branch, and the
+// derivative of the "GatedAttention [2025]" §1.2.1 SDPA equation, causal per
+// §1.4.1, for the attention branch).  For the upstream gradient dY' of the
+// gated output Y' = Y ⊙ g:
+//   prep:    dY = dY' ⊙ g (bf16), Dᵢ = Σ_d dY'·Y' (= Σ_d dY·Y, the gate cancels),
+//            dZ = dY' ⊙ Y' ⊙ (1 − g) (= dY' ⊙ Y ⊙ g(1 − g); headwise:
+//            (1 − g_h)·Dᵢ), so no division by g is needed.
+//   dQ:      per query tile, over its visible key tiles: S = Q·Kᵀ/√D,
+//            P = exp(S − LSE), dP = dY·Vᵀ, dS = P ⊙ (dP − D), dQ += dS·K/√D.
+//   dK, dV:  per key tile, over the query heads of its GQA group and the query
+//            tiles that see it: dV += Pᵀ·dY, dK += dSᵀ·Q/√D.
+// Two kernels recompute S and dP instead of one with atomics, so the result is
+// deterministic.
+//
+// Layout in LDS: every staged tile is [row][d] with a 272-byte row stride (one
+// 16-byte pad slot per row), filled by 16-byte direct loads.  Row reads (MFMA
+// operands with 8 consecutive d) are conflict-free; transposed reads
+// (ds_read_b64_tr_b16, operands with 8 consecutive rows) see 2-way conflicts.
+// The transposed-read addressing permutes rows inside each 16-row block so a
+// lane's 8 rows match the accumulator layout of S, exactly as the forward's PV
+// product does with its probabilities.
+#include <type_traits>
+
+#include "common.h"
+
+namespace gsa {
+
+#define GSA_LDS_B __attribute__((address_space(3)))
+
+namespace bwd {
+constexpr int QT = 128;   // query rows per dQ workgroup (4 waves x 32)
+constexpr int KT = 64;    // key rows per staged tile in the dQ kernel
+constexpr int KW = 128;   // key rows per dK/dV workgroup (4 waves x 32)
+constexpr int QW = 64;    // query rows per staged tile in the dK/dV kernel
+constexpr uint32_t kOOB = 0xfffffff0u;
+}  // namespace bwd
+
+enum : int { kBwdGateNone = 0, kBwdGateElem = 1, kBwdGateHead = 2 };
+
+// ---------------------------------------------------------------- prep
+// One (token, head) row per 16 threads, 8 head dims per thread.
+template <int D, int MODE>
+__global__ __launch_bounds__(256)
+void bwd_prep_kernel(const bf16* __restrict__ dYg, const bf16* __restrict__ Yg,
+                     const float* __restrict__ Gate, bf16* __restrict__ dY, float* __restrict__ Dv,
+                     bf16* __restrict__ dZ, int B, int S, int Hq) {
+  constexpr int TPR = D / 8;                 // threads per row
+  constexpr int RPB = 256 / TPR;             // rows per block
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;   // = token * Hq + head
+  const int part = tid % TPR;
+  const int64_t nrows = (int64_t)B * S * Hq;
+  const bool live = row < nrows;
+  const int64_t rr = live ? row : nrows - 1;
+  const int64_t tok = rr / Hq;
+  const int head = (int)(rr % Hq);
+  const int64_t e0 = rr * D + part * 8;
+  const u32x4 gy = *(const u32x4*)(dYg + e0);
+  const u32x4 yy = *(const u32x4*)(Yg + e0);
+  float g[8];
+  if constexpr (MODE == kBwdGateElem) {
+    const f32x4 g0 = *(const f32x4*)(Gate + e0);
+    const f32x4 g1 = *(const f32x4*)(Gate + e0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g[e] = g0[e];
+      g[e + 4] = g1[e];
+    }
+  } else {
+    const float gh = MODE == kBwdGateHead ? Gate[tok * Hq + head] : 1.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = gh;
+  }
+  float dsum = 0.f, dy[8], z[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a0 = bf16_lo(gy[w]), a1 = bf16_hi(gy[w]);
+    const float y0 = bf16_lo(yy[w]), y1 = bf16_hi(yy[w]);
+    const float p0 = a0 * y0, p1 = a1 * y1;
+    dsum += p0;
+    dsum += p1;
+    dy[2 * w] = a0 * g[2 * w];
+    dy[2 * w + 1] = a1 * g[2 * w + 1];
+    z[2 * w] = p0 * (1.0f - g[2 * w]);
+    z[2 * w + 1] = p1 * (1.0f - g[2 * w + 1]);
+  }
+  // row sum over the TPR threads of the row (fixed order)
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) dsum += __shfl_xor(dsum, o);
+  if (!live) return;
+  if constexpr (MODE != kBwdGateNone) {
+    *(u32x4*)(dY + e0) = u32x4{pack_bf16x2(dy[0], dy[1]), pack_bf16x2(dy[2], dy[3]),
+                               pack_bf16x2(dy[4], dy[5]), pack_bf16x2(dy[6], dy[7])};
+  }
+  if constexpr (MODE == kBwdGateElem) {
+    *(u32x4*)(dZ + e0) = u32x4{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]),
+                               pack_bf16x2(z[4], z[5]), pack_bf16x2(z[6], z[7])};
+  }
+  if (part == 0) {
+    const int64_t b = tok / S, i = tok % S;
+    Dv[(b * Hq + head) * S + i] = dsum;
+    if constexpr (MODE == kBwdGateHead) dZ[tok * Hq + head] = (bf16)((1.0f - g[0]) * dsum);
+  }
+}
+
+// ---------------------------------------------------------------- shared pieces
+// Staged tile: ROWS rows of D bf16, 272-byte (D=128) / 144-byte (D=64) stride.
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int SL = CH + 1;         // slots per row (one pad slot)
+  static constexpr int RSB = SL * 16;       // row stride in bytes
+};
+
+// Direct loads of `rows` rows of a [*, stride] bf16 tensor into a padded tile:
+// 4 waves, wave instruction i covers slots 64*i .. 64*i+63.  Rows at or past
+// `row_end` and the pad slot read zeros.
+template <int D, int ROWS>
+struct TileLoader {
+  static constexpr int SL = Tile<D>::SL;
+  static constexpr int NI = (ROWS * SL + 255) / 256;   // instructions per wave
+  uint32_t off[NI];
+  uint32_t ins_base[NI];
+  __device__ void init(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int ins = wave + 4 * j;
+      const int sl = ins * 64 + lane;
+      const int row = sl / SL, ch = sl % SL;
+      off[j] = (ch < Tile<D>::CH && row < ROWS) ? (uint32_t)row * row_bytes + ch * 16 : kOOBv();
+      ins_base[j] = (uint32_t)ins * 64 * 16;
+    }
+  }
+  static __device__ constexpr uint32_t kOOBv() { return 0xfffffff0u; }
+  // rows [r0, r0 + ROWS) of the tensor behind rs; rows >= row_end read zeros
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0, int row_end,
+                       uint32_t lds_base, int wave) const {
+    const uint32_t base = (uint32_t)r0 * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int ins = wave + 4 * j;
+      if (ins * 64 < ROWS * SL) {
+        const int lane_row = (int)((ins_base[j] / 16 + (threadIdx.x & 63)) / SL);
+        const bool ok = off[j] != kOOBv() && r0 + lane_row < row_end;
+        dma16_lds(rs, ok ? off[j] + base : kOOBv(), lds_base + ins_base[j]);
+      }
+    }
+  }
+};
+
+// Transposed-read address of a lane inside a padded tile for the A operand of
+// an MFMA whose k index runs over tile rows: rows 16t + 8a + 4*hl + 0..3 of a
+// 16-row block land in k slots 4a..4a+3 of lane half hl (the accumulator layout
+// of S), dims dt*32 + (lane within 32).
+template <int D>
+__device__ __forceinline__ uint32_t tr_base(int lane, int dt) {
+  const int vg = lane >> 4, vi = lane & 15;
+  const int r = 4 * (vg >> 1) + (vi >> 2);
+  const int dc = 16 * (vg & 1) + 4 * (vi & 3);
+  return (uint32_t)(r * Tile<D>::RSB + (dt * 32 + dc) * 2);
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const GSA_LDS_B char* p, int rsb) {
+  const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)p);
+  const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)(p + 8 * rsb));
+  bf16x8 a;
+  a.lo = __builtin_bit_cast(bf16x4, lo);
+  a.hi = __builtin_bit_cast(bf16x4, hi);
+  return a;
+}
+
+// Row read: row `row`, dims 16*kk + 8*hl .. +7 (the A operand of S-type products).
+template <int D>
+__device__ __forceinline__ bf16x8 row_read(const GSA_LDS_B char* tile, int row, int kk, int hl) {
+  return *(const GSA_LDS_B bf16x8*)(tile + row * Tile<D>::RSB + (2 * kk + hl) * 16);
+}
+
+// Accumulator pair (2 x 32 rows of a 64-row block, 16 regs each) -> bf16 B
+// operands, k order matching tr_base's row permutation.
+__device__ __forceinline__ void pack_b(const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[sub][t][e] = (bf16)s[sub][8 * t + e];
+}
+
+// ---------------------------------------------------------------- dQ
+// 256 threads: 128 query rows of one head (4 waves x 32); key tiles of 64.
+//   Sᵀ = K·Qᵀ, dPᵀ = V·dYᵀ  (A = K / V rows from LDS, B = Q / dY fragments)
+//   dQᵀ += Kᵀ·dSᵀ          (A = K through transposed reads, B = dS in bf16)
+template <int D>
+__global__ __launch_bounds__(256, 1)
+void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                   const bf16* __restrict__ dY, const float* __restrict__ Lse,
+                   const float* __restrict__ Dv, bf16* __restrict__ dQ, int B, int S, int Hq,
+                   int Hkv, int n_qtiles, float scale) {
+  using namespace bwd;
+  constexpr int RSB = Tile<D>::RSB;
+  __shared__ __align__(16) char Ks[2][KT * RSB];
+  __shared__ __align__(16) char Vs[2][KT * RSB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int bid = blockIdx.x;
+  const int hb = Hq * B;
+  const int qt = n_qtiles - 1 - bid / hb;
+  const int pair = bid % hb;
+  const int head = pair % Hq, b = pair / Hq;
+  const int kvh = head / (Hq / Hkv);
+  const int q0 = qt * QT, qw0 = q0 + wave * 32, my_q = qw0 + l32;
+  const int64_t q_row = (int64_t)Hq * D, kv_row = (int64_t)Hkv * D;
+  const float scale_log2 = scale * kLog2e;
+
+  // Q and dY fragments (B operands), LSE (base 2) and D of this lane's row
+  bf16x8 qf[D / 16], yf[D / 16];
+  {
+    const auto qr = make_rsrc(Q + (int64_t)b * S * q_row + (int64_t)head * D,
+                              (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2));
+    const auto yr = make_rsrc(dY + (int64_t)b * S * q_row + (int64_t)head * D,
+                              (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2));
+    const uint32_t o = (uint32_t)(((int64_t)my_q * q_row + 8 * hl) * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(qr, o + 32 * kk, 0));
+      yf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(yr, o + 32 * kk, 0));
+    }
+  }
+  const int qc = min(my_q, S - 1);
+  const float lse2 = Lse[((int64_t)b * Hq + head) * S + qc] * kLog2e;
+  const float dval = Dv[((int64_t)b * Hq + head) * S + qc];
+
+  const uint32_t row_b = (uint32_t)(kv_row * 2);
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)S * kv_row - (int64_t)kvh * D) * 2);
+  const auto krs = make_rsrc(K + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+  const auto vrs = make_rsrc(V + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+  TileLoader<D, KT> ld;
+  ld.init(wave, lane, row_b);
+  uint32_t ks_lds[2], vs_lds[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ks_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[i][0]));
+    vs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[i][0]));
+  }
+  uint32_t trb[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+  const int kv_end = min(S, q0 + QT);
+  const int n_kv = ceil_div(kv_end, KT);
+  ld.load(krs, row_b, 0, S, ks_lds[0], wave);
+  ld.load(vrs, row_b, 0, S, vs_lds[0], wave);
+  for (int it = 0; it < n_kv; ++it) {
+    const int buf = it & 1, k0 = it * KT;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < n_kv) {
+      ld.load(krs, row_b, k0 + KT, S, ks_lds[buf ^ 1], wave);
+      ld.load(vrs, row_b, k0 + KT, S, vs_lds[buf ^ 1], wave);
+    }
+    const GSA_LDS_B char* kt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ks[buf][0];
+    const GSA_LDS_B char* vt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Vs[buf][0];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[sub][r] = 0.f;
+        dp[sub][r] = 0.f;
+      }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = mfma32x32x16(row_read<D>(kt, sub * 32 + l32, kk, hl), qf[kk], s[sub]);
+        dp[sub] = mfma32x32x16(row_read<D>(vt, sub * 32 + l32, kk, hl), yf[kk], dp[sub]);
+      }
+    // element (sub, r) is key k0 + sub*32 + 8*(r/4) + 4*hl + r%4 of query my_q
+    const bool masked = (k0 + KT - 1 > qw0) || (k0 + KT > S);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool vis = !masked || (key <= qc && key < S);
+        const float p = vis ? fast_exp2(fmaf(s[sub][r], scale_log2, -lse2)) : 0.f;
+        s[sub][r] = p * (dp[sub][r] - dval);   // dS
+      }
+    bf16x8 ds[2][2];
+    pack_b(s, ds);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = mfma32x32x16(tr_read(kt + trb[dt] + (sub * 32 + 16 * t) * RSB, RSB), ds[sub][t], acc[dt]);
+  }
+
+  if (my_q >= S) return;
+  bf16* out = dQ + ((int64_t)b * S + my_q) * q_row + (int64_t)head * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = dt * 32 + 8 * i + 4 * hl;
+      *(u32x2*)(out + d0) = u32x2{pack_bf16x2(acc[dt][4 * i] * scale, acc[dt][4 * i + 1] * scale),
+                                  pack_bf16x2(acc[dt][4 * i + 2] * scale, acc[dt][4 * i + 3] * scale)};
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// 256 threads: 128 keys of one key/value head (4 waves x 32).  For each query
+// head of the group and each 64-row query tile that sees these keys:
+//   S = Q·Kᵀ, dP = dY·Vᵀ      (A = Q / dY rows from LDS, B = K / V fragments)
+//   dVᵀ += dYᵀ·P, dKᵀ += Qᵀ·dS (A through transposed reads, B = P / dS in bf16)
+template <int D>
+__global__ __launch_bounds__(256, 1)
+void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                     const bf16* __restrict__ dY, const float* __restrict__ Lse,
+                     const float* __restrict__ Dv, bf16* __restrict__ dK, bf16* __restrict__ dV,
+                     int B, int S, int Hq, int Hkv, int n_ktiles, float scale) {
+  using namespace bwd;
+  constexpr int RSB = Tile<D>::RSB;
+  __shared__ __align__(16) char Qs[2][QW * RSB];
+  __shared__ __align__(16) char Ys[2][QW * RSB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int bid = blockIdx.x;
+  const int hb = Hkv * B;
+  const int kt_i = bid / hb;                       // light (early) key tiles have the most work: first
+  const int pair = bid % hb;
+  const int kvh = pair % Hkv, b = pair / Hkv;
+  const int G = Hq / Hkv;
+  const int k0 = kt_i * KW, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  const int64_t q_row = (int64_t)Hq * D, kv_row = (int64_t)Hkv * D;
+  const float scale_log2 = scale * kLog2e;
+
+  // K and V fragments (B operands) of this lane's key
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const uint32_t kv_bytes = (uint32_t)(((int64_t)S * kv_row - (int64_t)kvh * D) * 2);
+    const auto kr = make_rsrc(K + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+    const auto vr = make_rsrc(V + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+    const uint32_t o = (uint32_t)(((int64_t)my_k * kv_row + 8 * hl) * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(kr, o + 32 * kk, 0));
+      vf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(vr, o + 32 * kk, 0));
+    }
+  }
+  const uint32_t row_b = (uint32_t)(q_row * 2);
+  TileLoader<D, QW> ld;
+  ld.init(wave, lane, row_b);
+  uint32_t qs_lds[2], ys_lds[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    qs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Qs[i][0]));
+    ys_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ys[i][0]));
+  }
+  uint32_t trb[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+
+  // query tiles that see keys [k0, k0 + KW): rows >= k0
+  const int qt_first = k0 / QW;
+  const int n_qt = ceil_div(S, QW) - qt_first;
+  const int n_steps = G * max(n_qt, 0);
+  auto tile_of = [&](int step, int& head, int& qs0) {
+    head = kvh * G + step / n_qt;
+    qs0 = (qt_first + step % n_qt) * QW;
+  };
+  auto issue = [&](int step, int buf) {
+    int head, qs0;
+    tile_of(step, head, qs0);
+    const uint32_t bytes = (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2);
+    const auto qr = make_rsrc(Q + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
+    const auto yr = make_rsrc(dY + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
+    ld.load(qr, row_b, qs0, S, qs_lds[buf], wave);
+    ld.load(yr, row_b, qs0, S, ys_lds[buf], wave);
+  };
+  if (n_steps > 0) issue(0, 0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    int head, qs0;
+    tile_of(step, head, qs0);
+    // LSE (base 2) and D of the 2x16 query rows this lane's registers hold:
+    // row qs0 + 32*sub + 8*(r/4) + 4*hl + r%4
+    float lse2[2][16], dval[2][16];
+    {
+      const float* lrow = Lse + ((int64_t)b * Hq + head) * S;
+      const float* drow = Dv + ((int64_t)b * Hq + head) * S;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = min(qs0 + 32 * sub + 8 * (r >> 2) + 4 * hl + (r & 3), S - 1);
+          lse2[sub][r] = lrow[qrow] * kLog2e;
+          dval[sub][r] = drow[qrow];
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (step + 1 < n_steps) issue(step + 1, buf ^ 1);
+    const GSA_LDS_B char* qt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Qs[buf][0];
+    const GSA_LDS_B char* yt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ys[buf][0];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[sub][r] = 0.f;
+        dp[sub][r] = 0.f;
+      }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = mfma32x32x16(row_read<D>(qt, sub * 32 + l32, kk, hl), kf[kk], s[sub]);
+        dp[sub] = mfma32x32x16(row_read<D>(yt, sub * 32 + l32, kk, hl), vf[kk], dp[sub]);
+      }
+    // element (sub, r): query qs0 + 32*sub + 8*(r/4) + 4*hl + r%4, key my_k
+    f32x16 ds[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = qs0 + 32 * sub + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool vis = my_k <= qrow && qrow < S && my_k < S;
+        const float p = vis ? fast_exp2(fmaf(s[sub][r], scale_log2, -lse2[sub][r])) : 0.f;
+        ds[sub][r] = p * (dp[sub][r] - dval[sub][r]);
+        s[sub][r] = p;
+      }
+    bf16x8 pb[2][2], db[2][2];
+    pack_b(s, pb);
+    pack_b(ds, db);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int ro = (sub * 32 + 16 * t) * RSB;
+          dv[dt] = mfma32x32x16(tr_read(yt + trb[dt] + ro, RSB), pb[sub][t], dv[dt]);
+          dk[dt] = mfma32x32x16(tr_read(qt + trb[dt] + ro, RSB), db[sub][t], dk[dt]);
+        }
+  }
+
+  if (my_k >= S) return;
+  bf16* ok = dK + ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
+  bf16* ov = dV + ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = dt * 32 + 8 * i + 4 * hl;
+      *(u32x2*)(ok + d0) = u32x2{pack_bf16x2(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale),
+                                 pack_bf16x2(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale)};
+      *(u32x2*)(ov + d0) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
+                                 pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+    }
+}
+
+// ---------------------------------------------------------------- launch
+template <int D>
+static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* dYg,
+                               const void* Yg, const float* G, const float* Lse, void* dQ, void* dK,
+                               void* dV, void* dY, float* Dv, void* dZ, int B, int S, int Hq, int Hkv,
+                               int mode, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const int64_t rows = (int64_t)B * S * Hq;
+  const int rpb = 256 / (D / 8);
+  const unsigned pblocks = (unsigned)((rows + rpb - 1) / rpb);
+  const bf16* dy_attn = (const bf16*)dY;
+  if (mode == kBwdGateElem)
+    hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateElem>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
+                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+  else if (mode == kBwdGateHead)
+    hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateHead>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
+                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+  else {
+    hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateNone>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
+                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+    dy_attn = (const bf16*)dYg;   // no gate: the SDPA output's gradient is dY' itself
+  }
+  const int nq = ceil_div(S, bwd::QT);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((int64_t)nq * Hq * B)), dim3(256), 0, st,
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, Lse, (const float*)Dv,
+                     (bf16*)dQ, B, S, Hq, Hkv, nq, scale);
+  const int nk = ceil_div(S, bwd::KW);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)((int64_t)nk * Hkv * B)), dim3(256), 0, st,
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, Lse, (const float*)Dv,
+                     (bf16*)dK, (bf16*)dV, B, S, Hq, Hkv, nk, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
+                           const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
+                           float* Dv, void* dZ, int B, int S, int Hq, int Hkv, int D, int mode,
+                           hipStream_t stream) {
+  if (D == 128)
+    return launch_bwd_d<128>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Dv, dZ, B, S, Hq, Hkv, mode, stream);
+  return launch_bwd_d<64>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Dv, dZ, B, S, Hq, Hkv, mode, stream);
+}
+
+}  // namespace gsa

@@ -37,6 +37,7 @@
 namespace gsa {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr float kLn2 = 0.69314718055994531f;
 
 namespace fwd {
 constexpr int BM = 128;  // query rows per workgroup
@@ -55,8 +56,8 @@ template <int D, int MODE, int QB>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1)
 void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                           const bf16* __restrict__ V, const float* __restrict__ Gate,
-                          bf16* __restrict__ Y, int B, int S, int Hq, int Hkv, int n_qtiles,
-                          float scale_log2) {
+                          bf16* __restrict__ Y, float* __restrict__ Lse, int B, int S, int Hq,
+                          int Hkv, int n_qtiles, float scale_log2) {
   using namespace fwd;
   constexpr int BMQ = BM * QB;    // query rows per workgroup (QB blocks of 32 per wave)
   constexpr int CH = D / 8;       // 16-byte chunks per K/V row
@@ -402,6 +403,10 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     // every lane takes part in the exchange; rows past the end store nothing
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);  // the two halves summed different keys
     if (my_q[qb] >= S) continue;
+    // log-sum-exp of the row's scaled scores (natural log): m and l are in the
+    // base-2 domain of s·log2(e), so ln Σ e^s = (m + log2 l)·ln 2
+    if (Lse != nullptr && hl == 0)
+      Lse[((int64_t)b * Hq + head) * S + my_q[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
     const float inv = 1.0f / l_tot;
     const int64_t tok = (int64_t)b * S + my_q[qb];
     bf16* yrow = Y + tok * q_row + (int64_t)head * D;
@@ -435,8 +440,8 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, const float* __restrict__ Gate,
-                         float* __restrict__ Y, int B, int S, int Skv, int Hq, int Hkv,
-                         int n_qtiles, float scale_log2) {
+                         float* __restrict__ Y, float* __restrict__ Lse, int B, int S, int Skv,
+                         int Hq, int Hkv, int n_qtiles, float scale_log2) {
   constexpr int BMF = 64, BNF = 32, DPL = D / 4, LDF = D + 4;
   __shared__ float Ks[BNF * LDF];
   __shared__ float Vs[BNF * LDF];
@@ -504,6 +509,8 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   }
   if (q >= S) return;
   const float inv = 1.0f / l_run;
+  if (Lse != nullptr && part == 0)
+    Lse[((int64_t)b * Hq + head) * S + q] = (m_run + log2f(l_run)) * kLn2;
   const int64_t tok = (int64_t)b * S + q;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
@@ -517,48 +524,49 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 
 template <int D, int MODE, int QB = GSA_FWD_QB>
 static void launch_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
-                        int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st) {
+                        float* Lse, int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st) {
   const int nq = ceil_div(S, fwd::BM * QB);
   const int64_t blocks = (int64_t)nq * Hq * B;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE, QB>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, B, S, Hq, Hkv,
-                     nq, scale_log2);
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, Lse, B, S, Hq,
+                     Hkv, nq, scale_log2);
 }
 
 template <int D, int MODE>
 static void launch_f32(const void* Q, const void* K, const void* V, const float* G, void* Y,
-                       int B, int S, int Skv, int Hq, int Hkv, float scale_log2, hipStream_t st) {
+                       float* Lse, int B, int S, int Skv, int Hq, int Hkv, float scale_log2,
+                       hipStream_t st) {
   const int nq = ceil_div(S, 64);
   const int64_t blocks = (int64_t)nq * Hq * B;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, MODE>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const float*)Q, (const float*)K, (const float*)V, G, (float*)Y, B, S, Skv,
-                     Hq, Hkv, nq, scale_log2);
+                     (const float*)Q, (const float*)K, (const float*)V, G, (float*)Y, Lse, B, S,
+                     Skv, Hq, Hkv, nq, scale_log2);
 }
 
 template <int D>
 static void dispatch_mode(int mode, bool bf16_inputs, const void* Q, const void* K, const void* V,
-                          const float* G, void* Y, int B, int S, int Skv, int Hq, int Hkv,
-                          float scale_log2, hipStream_t st) {
+                          const float* G, void* Y, float* Lse, int B, int S, int Skv, int Hq,
+                          int Hkv, float scale_log2, hipStream_t st) {
   if (bf16_inputs) {
-    if (mode == kGateElem) launch_bf16<D, kGateElem>(Q, K, V, G, Y, B, S, Hq, Hkv, scale_log2, st);
-    else if (mode == kGateHead) launch_bf16<D, kGateHead>(Q, K, V, G, Y, B, S, Hq, Hkv, scale_log2, st);
-    else launch_bf16<D, kGateNone>(Q, K, V, G, Y, B, S, Hq, Hkv, scale_log2, st);
+    if (mode == kGateElem) launch_bf16<D, kGateElem>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, st);
+    else if (mode == kGateHead) launch_bf16<D, kGateHead>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, st);
+    else launch_bf16<D, kGateNone>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, st);
   } else {
-    if (mode == kGateElem) launch_f32<D, kGateElem>(Q, K, V, G, Y, B, S, Skv, Hq, Hkv, scale_log2, st);
-    else if (mode == kGateHead) launch_f32<D, kGateHead>(Q, K, V, G, Y, B, S, Skv, Hq, Hkv, scale_log2, st);
-    else launch_f32<D, kGateNone>(Q, K, V, G, Y, B, S, Skv, Hq, Hkv, scale_log2, st);
+    if (mode == kGateElem) launch_f32<D, kGateElem>(Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, st);
+    else if (mode == kGateHead) launch_f32<D, kGateHead>(Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, st);
+    else launch_f32<D, kGateNone>(Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, st);
   }
 }
 
 // bf16 inputs require Skv == S (prefill); float32 inputs allow Skv >= S.
 hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const float* G, void* Y,
-                           int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
+                           float* Lse, int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
                            bool bf16_inputs, hipStream_t stream) {
   const float scale_log2 = kLog2e / sqrtf((float)D);
   if (D == 128)
-    dispatch_mode<128>(mode, bf16_inputs, Q, K, V, G, Y, B, S, Skv, Hq, Hkv, scale_log2, stream);
+    dispatch_mode<128>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
   else
-    dispatch_mode<64>(mode, bf16_inputs, Q, K, V, G, Y, B, S, Skv, Hq, Hkv, scale_log2, stream);
+    dispatch_mode<64>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
   return hipGetLastError();
 }
 

@@ -1,0 +1,263 @@
+// Gate-branch products of the backward (bf16 operands, fp32 accumulation):
+//   dX   = dZ · W_θᵀ     [M, d_model]  (bf16 out)
+//   dW_θ = Xᵀ · dZ       [d_model, N]  (fp32 out)
+// for the gate-score gradient dZ [M, N] (the "Gated Attention如何用1%的参数量…"
+// page, §2.2 gradient analysis: the gate input's gradient times the projection's
+// transposes).  X is [M, d_model] and W_θ is [d_model, N], both row-major.
+//
+// One kernel serves both: out[m][n] = Σ_k L[m][k] · R[k][n] where each operand
+// is either k-contiguous in memory or m/n-contiguous.  dX has both operands
+// k-contiguous (dZ rows, W_θ rows); dW_θ has both m/n-contiguous (X and dZ read
+// down their token columns).  Tiles of 128 (m) x 128 (n) x 64 (k), 4 waves in a
+// 2x2 grid of 64x64, double-buffered in LDS by 16-byte direct loads.  A
+// k-contiguous operand is staged as [m|n][k] and read row-wise (8 consecutive
+// k per lane); an m/n-contiguous one as [k][m|n] and read with transposed LDS
+// reads, which hand each lane 4 consecutive k of one column.  Padding keeps
+// both read kinds free of bank conflicts.  The MFMA's row index is n, so each
+// lane ends with 4 consecutive output columns (one vector store).
+//
+// dW_θ sums over all M tokens; when its output tiles alone cannot fill the chip
+// the token range is cut into equal chunks whose partial sums go to a
+// workspace and are added in chunk order by a second kernel (deterministic).
+#include "common.h"
+
+namespace gsa {
+
+#define GSA_LDS_G __attribute__((address_space(3)))
+
+namespace bgemm {
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr uint32_t kOOB = 0xfffffff0u;
+
+// Staged operand tile.  KC: 128 rows (m or n) of 64 k, 9 slots of 16 B per row
+// (one pad slot).  MC: 64 rows (k) of 128 m/n, 20 slots per row (4 pad slots:
+// a 320-byte stride puts the four rows of a transposed read 16 banks apart).
+template <bool KC>
+struct Stage {
+  static constexpr int ROWS = KC ? 128 : 64;
+  static constexpr int CH = KC ? 8 : 16;
+  static constexpr int SL = KC ? 9 : 20;
+  static constexpr int RSB = SL * 16;
+  static constexpr int SLOTS = ROWS * SL;
+  static constexpr int NI = (SLOTS + 255) / 256;   // direct-load instructions per wave
+  static constexpr int BYTES = SLOTS * 16;
+};
+
+template <bool KC>
+struct Loader {
+  using St = Stage<KC>;
+  int row[St::NI], ch[St::NI];   // ch < 0: pad slot or no slot
+  __device__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < St::NI; ++j) {
+      const int sl = (wave + 4 * j) * 64 + lane;
+      row[j] = sl / St::SL;
+      const int c = sl % St::SL;
+      ch[j] = (sl < St::SLOTS && c < St::CH) ? c : -1;
+    }
+  }
+  // Tile at (mn0, k0) of an operand with leading dimension ld (elements),
+  // valid m/n indices < mn_end and k indices < k_end; the rest reads zeros.
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t lds, int mn0, int mn_end, int k0, int k_end,
+                       uint32_t ld, int wave) const {
+#pragma unroll
+    for (int j = 0; j < St::NI; ++j) {
+      const int ins = wave + 4 * j;
+      if (ins * 64 < St::SLOTS) {
+        bool ok;
+        uint32_t off;
+        if constexpr (KC) {
+          const int mn = mn0 + row[j], k = k0 + 8 * ch[j];
+          ok = ch[j] >= 0 && mn < mn_end && k < k_end;
+          off = ((uint32_t)mn * ld + (uint32_t)k) * 2u;
+        } else {
+          const int k = k0 + row[j], mn = mn0 + 8 * ch[j];
+          ok = ch[j] >= 0 && k < k_end && mn < mn_end;
+          off = ((uint32_t)k * ld + (uint32_t)mn) * 2u;
+        }
+        dma16_lds(rs, ok ? off : kOOB, lds + (uint32_t)ins * 1024u);
+      }
+    }
+  }
+};
+
+// MFMA operand (32 m/n values at col0 + l32, k = 16*ks + 8*hl .. +7) from a tile.
+template <bool KC>
+__device__ __forceinline__ bf16x8 frag(const GSA_LDS_G char* tile, int col0, int ks, int lane_off) {
+  if constexpr (KC) {
+    return *(const GSA_LDS_G bf16x8*)(tile + col0 * Stage<true>::RSB + ks * 32 + lane_off);
+  } else {
+    const GSA_LDS_G char* p = tile + ks * 16 * Stage<false>::RSB + col0 * 2 + lane_off;
+    const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_G i16x4*)p);
+    const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_G i16x4*)(p + 4 * Stage<false>::RSB));
+    bf16x8 a;
+    a.lo = __builtin_bit_cast(bf16x4, lo);
+    a.hi = __builtin_bit_cast(bf16x4, hi);
+    return a;
+  }
+}
+
+// Lane part of a fragment address.  KC: row l32, chunk hl.  MC: in each 16-lane
+// group g, lane i names k row 8*(g/2) + i/4 and columns 16*(g%2) + 4*(i%4) .. +3,
+// and receives column 16*(g%2) + i at the four k rows 8*(g/2) + 0..3 (and, from
+// the second read 4 rows down, + 4..7): MFMA row l32, k slots 8*hl + 0..7.
+template <bool KC>
+__device__ __forceinline__ int frag_lane_off(int lane) {
+  if constexpr (KC) {
+    return (lane & 31) * Stage<true>::RSB + (lane >> 5) * 16;
+  } else {
+    const int g = lane >> 4, i = lane & 15;
+    return (8 * (g >> 1) + (i >> 2)) * Stage<false>::RSB + (16 * (g & 1) + 4 * (i & 3)) * 2;
+  }
+}
+}  // namespace bgemm
+
+template <typename OutT, bool L_KC, bool R_KC>
+__global__ __launch_bounds__(256, 2)
+void bwd_gemm_kernel(const bf16* __restrict__ L, const bf16* __restrict__ R, OutT* __restrict__ out,
+                     int M, int N, int K, uint32_t ldl, uint32_t ldr, uint32_t l_bytes, uint32_t r_bytes,
+                     int tiles_m, int tiles_n, int k_chunk) {
+  using namespace bgemm;
+  __shared__ __align__(16) char Ls[2][Stage<L_KC>::BYTES];
+  __shared__ __align__(16) char Rs[2][Stage<R_KC>::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int tiles = tiles_m * tiles_n;
+  const int z = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int tm = t / tiles_n, tn = t % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = z * k_chunk, ke = min(K, kb + k_chunk);
+  OutT* outz = out + (int64_t)z * M * N;
+
+  const auto lrs = make_rsrc(L, l_bytes);
+  const auto rrs = make_rsrc(R, r_bytes);
+  Loader<L_KC> lld;
+  Loader<R_KC> rld;
+  lld.init(wave, lane);
+  rld.init(wave, lane);
+  uint32_t l_lds[2], r_lds[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    l_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ls[i][0]));
+    r_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Rs[i][0]));
+  }
+  const int l_off = frag_lane_off<L_KC>(lane), r_off = frag_lane_off<R_KC>(lane);
+
+  f32x16 acc[2][2];   // [n block][m block]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = ke > kb ? ceil_div(ke - kb, BK) : 0;
+  if (nk > 0) {
+    lld.load(lrs, l_lds[0], m0, M, kb, ke, ldl, wave);
+    rld.load(rrs, r_lds[0], n0, N, kb, ke, ldr, wave);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) {
+      const int k0 = kb + (kt + 1) * BK;
+      lld.load(lrs, l_lds[buf ^ 1], m0, M, k0, ke, ldl, wave);
+      rld.load(rrs, r_lds[buf ^ 1], n0, N, k0, ke, ldr, wave);
+    }
+    const GSA_LDS_G char* lt = (const GSA_LDS_G char*)(GSA_LDS_G void*)&Ls[buf][0];
+    const GSA_LDS_G char* rt = (const GSA_LDS_G char*)(GSA_LDS_G void*)&Rs[buf][0];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = frag<R_KC>(rt, wn * 64 + 32 * i, ks, r_off);
+        b[i] = frag<L_KC>(lt, wm * 64 + 32 * i, ks, l_off);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // lane holds output row m0 + wm*64 + 32*j + l32 and columns
+  // n0 + wn*64 + 32*i + 8*(r/4) + 4*hl + 0..3 (N is a multiple of 4)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + wm * 64 + 32 * j + l32;
+    if (m >= M) continue;
+    OutT* orow = outz + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + 32 * i + 8 * q + 4 * hl;
+        if (n >= N) continue;
+        const f32x16& c = acc[i][j];
+        if constexpr (std::is_same<OutT, float>::value) {
+          *(f32x4*)(orow + n) = f32x4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+        } else {
+          *(u32x2*)(orow + n) = u32x2{pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3])};
+        }
+      }
+  }
+}
+
+// out[i] = Σ_z part[z][i] in z order (float4 granules; n4 = element count / 4).
+__global__ __launch_bounds__(256)
+void sum_partials_kernel(const f32x4* __restrict__ part, f32x4* __restrict__ out, int64_t n4, int splits) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 s = part[i];
+    for (int z = 1; z < splits; ++z) s += part[(int64_t)z * n4 + i];
+    out[i] = s;
+  }
+}
+
+// Token chunks for dW_θ: enough workgroups to fill the chip (about 1024), each
+// chunk a multiple of 64 tokens and at least 256 of them.
+int64_t bwd_dw_splits(int64_t M, int64_t d_model, int64_t N) {
+  const int64_t tiles = ceil_div<int64_t>(d_model, bgemm::BM) * ceil_div<int64_t>(N, bgemm::BN);
+  int64_t s = ceil_div<int64_t>(1024, tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, M / 256));
+  return std::max<int64_t>(s, 1);
+}
+int64_t bwd_dw_chunk(int64_t M, int64_t splits) {
+  return ceil_div<int64_t>(ceil_div<int64_t>(M, splits), bgemm::BK) * bgemm::BK;
+}
+
+// dX[M, d_model] = dZ[M, N] · W_θ[d_model, N]ᵀ  (both operands k-contiguous, k = N)
+hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
+                              int64_t N, hipStream_t st) {
+  const int tm = (int)ceil_div<int64_t>(M, bgemm::BM), tn = (int)ceil_div<int64_t>(d_model, bgemm::BN);
+  hipLaunchKernelGGL((bwd_gemm_kernel<bf16, true, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, st,
+                     (const bf16*)dZ, (const bf16*)W, (bf16*)dX, (int)M, (int)d_model, (int)N,
+                     (uint32_t)N, (uint32_t)N, (uint32_t)(M * N * 2), (uint32_t)(d_model * N * 2), tm, tn,
+                     (int)N);
+  return hipGetLastError();
+}
+
+// dW_θ[d_model, N] = X[M, d_model]ᵀ · dZ[M, N]  (both operands m/n-contiguous, k = M);
+// partials: splits * d_model * N floats when splits > 1 (else unused)
+hipError_t launch_bwd_gemm_dw(const void* X, const void* dZ, float* dW, float* partials, int64_t M,
+                              int64_t d_model, int64_t N, int64_t splits, hipStream_t st) {
+  const int tm = (int)ceil_div<int64_t>(d_model, bgemm::BM), tn = (int)ceil_div<int64_t>(N, bgemm::BN);
+  const int64_t chunk = bwd_dw_chunk(M, splits);
+  float* dst = splits > 1 ? partials : dW;
+  hipLaunchKernelGGL((bwd_gemm_kernel<float, false, false>), dim3((unsigned)(tm * tn * splits)), dim3(256), 0,
+                     st, (const bf16*)X, (const bf16*)dZ, dst, (int)d_model, (int)N, (int)M,
+                     (uint32_t)d_model, (uint32_t)N, (uint32_t)(M * d_model * 2), (uint32_t)(M * N * 2), tm,
+                     tn, (int)chunk);
+  if (splits > 1) {
+    const int64_t n4 = d_model * N / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div<int64_t>(n4, 256), 4096);
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(blocks), dim3(256), 0, st, (const f32x4*)partials, (f32x4*)dW,
+                       n4, (int)splits);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gsa

@@ -75,6 +75,26 @@ def forward(Q, K, V, G, mode, Y=None, stream=None):
     return Y
 
 
+def forward_lse(Q, K, V, G, mode, Y=None, LSE=None, stream=None):
+    """forward() that also returns the per-row log-sum-exp LSE [B, Hq, S] float32."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    if LSE is None:
+        LSE = torch.empty((B, Hq, S), dtype=torch.float32, device=Q.device)
+    elif LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S:
+        raise ValueError("LSE must be float32 with B*Hq*S elements")
+    gp = None if G is None else _dev(G, "G")
+    lib = _lib.load()
+    _lib.check(lib.gsa_forward_lse(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), gp, _dev(Y, "Y"),
+                                   _dev(LSE, "LSE"), B, S, Hq, Hkv, D, _mode(mode),
+                                   _dtype(Q, K, V, Y), _stream(stream)))
+    return Y, LSE
+
+
 def decode_num_splits(B, L, Hq, Hkv, D, num_splits=0):
     return int(_lib.load().gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits))
 
@@ -104,6 +124,47 @@ def decode(Q, Kc, Vc, G, mode, num_splits=0, Y=None, workspace=None, stream=None
                               B, L, Hq, Hkv, D, _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits,
                               wp, wbytes, _stream(stream)))
     return Y
+
+
+def backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, mode):
+    return int(_lib.load().gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, _mode(mode)))
+
+
+def backward(X, W, G, Q, K, V, Y, LSE, dY, mode, workspace=None, stream=None):
+    """Gradients of the gated forward for the upstream gradient dY of Y'.
+
+    X [..., d_model] and W [d_model, N] are the gate projection's inputs, G its
+    float32 output (from gate_logits), Y and LSE the outputs of forward_lse.  For
+    mode "none" X, W and G are None.  Returns a dict with dQ, dK, dV (shapes of
+    Q, K, V, bf16), dX (shape of X, bf16) and dW (float32 [d_model, N]); the
+    last two are None without a gate.
+    """
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
+    if Y.shape != Q.shape or dY.shape != Q.shape:
+        raise ValueError("Y and dY must have Q's shape")
+    if LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S:
+        raise ValueError("LSE must be float32 with B*Hq*S elements")
+    gated = mode != "none"
+    d_model = X.shape[-1] if gated else 0
+    if gated and (W.shape[0] != d_model or X.numel() != B * S * d_model):
+        raise ValueError("X must hold B*S rows of d_model and W must be [d_model, N]")
+    need = backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dX = torch.empty_like(X) if gated else None
+    dW = torch.empty(tuple(W.shape), dtype=torch.float32, device=Q.device) if gated else None
+    p = lambda t, n: None if t is None else _dev(t, n)
+    lib = _lib.load()
+    _lib.check(lib.gsa_backward(
+        p(X, "X"), p(W, "W"), p(G, "G"), _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(Y, "Y"),
+        _dev(LSE, "LSE"), _dev(dY, "dY"), p(dX, "dX"), p(dW, "dW"), _dev(dQ, "dQ"), _dev(dK, "dK"),
+        _dev(dV, "dV"), B, S, Hq, Hkv, D, d_model, _mode(mode), _dtype(Q, K, V, Y, dY),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dX, "dW": dW}
 
 
 def gated_attention(X, W, Q, K, V, mode, stream=None):

@@ -95,6 +95,17 @@ gsa_status gsa_forward(const void* Q, const void* K, const void* V, const float*
                        int mode, int dtype, void* stream);
 
 /*
+ * gsa_forward that also writes, for the backward, each row's log-sum-exp of
+ * its scaled scores over the visible keys ("GatedAttention [2025]" §1.2.1
+ * SDPA equation, causal per §1.4.1):
+ *   LSE : [B, Hq, S] float32 output, LSE[b,h,i] = ln Σ_{j<=i} exp(Q[b,i,h,:]·K[b,j,c,:] / √D)
+ *         (4-byte aligned).  The other arguments are gsa_forward's.
+ */
+gsa_status gsa_forward_lse(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                           float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                           int mode, int dtype, void* stream);
+
+/*
  * Split count gsa_decode will use for these sizes: num_splits itself if > 0,
  * otherwise the automatic choice.  Returns 0 for invalid sizes.
  */
@@ -125,6 +136,45 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
                       int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
                       int mode, int dtype, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes gsa_backward needs for these sizes (0 for invalid sizes;
+ * d_model is ignored for GSA_GATE_NONE).
+ */
+size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t d_model, int mode);
+
+/*
+ * Backward of the gated prefill path for an upstream gradient dY of Y'.  The
+ * gradients are the chain rule on the forward: through the product
+ * Y' = Y ⊙ g to the SDPA output and to the gate, through σ (σ' = σ(1 − σ)) to
+ * the gate scores Z = X·W_θ and through the projection to X and W_θ (the
+ * "Gated Attention如何用1%的参数量…" page, §2.2 gradient analysis), and
+ * through the causal softmax attention ("GatedAttention [2025]" §1.2.1 SDPA
+ * equation, causal per §1.4.1) to Q, K and V, with K and V gradients summed
+ * over each GQA group (§1.3.1).
+ *   X  : [B*S, d_model] bf16   W : [d_model, N] bf16   G : [B*S, N] float32,
+ *        the σ(X·W_θ) the forward used (gsa_gate_logits output);
+ *        N = Hq*D (ELEMENTWISE) or Hq (HEADWISE).  All three NULL iff mode is
+ *        GSA_GATE_NONE.
+ *   Q, K, V, Y, LSE : the forward's inputs and its outputs from gsa_forward_lse
+ *        (Y is the gated output Y').
+ *   dY : [B, S, Hq, D] bf16 upstream gradient.
+ *   outputs (overwritten, never accumulated into):
+ *        dQ [B, S, Hq, D], dK and dV [B, S, Hkv, D] (bf16);
+ *        dX [B*S, d_model] bf16, the gate projection's contribution to the
+ *        gradient of X (a caller that also projects Q, K, V from X adds its own);
+ *        dW [d_model, N] float32.  dX and dW are NULL iff mode is GSA_GATE_NONE.
+ *   workspace: device scratch of at least gsa_backward_workspace_bytes(...)
+ *        bytes, 16-byte aligned; contents on entry do not matter.
+ * Requires dtype GSA_BF16, D in {64, 128}, Hq % Hkv == 0, and with a gate
+ * d_model % 8 == 0 and N % 8 == 0.  The results are deterministic (no atomics).
+ */
+gsa_status gsa_backward(const void* X, const void* W, const float* G, const void* Q, const void* K,
+                        const void* V, const void* Y, const float* LSE, const void* dY, void* dX,
+                        float* dW, void* dQ, void* dK, void* dV, int64_t B, int64_t S, int64_t Hq,
+                        int64_t Hkv, int64_t D, int64_t d_model, int mode, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -52,6 +52,15 @@ def make_inputs(cfg: Config, seed: int = 0, device="cpu"):
     return {"X": X, "W": W, "Q": Q, "K": K, "V": V}
 
 
+def make_grad(cfg: Config, seed: int = 0, device="cpu"):
+    """Upstream gradient dY' [B,S,Hq,D] ~ N(0,1) in the config's dtype, from its own
+    generator seeded with ``seed + 1_000_003`` (independent of make_inputs' draws)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 1_000_003)
+    return _randn((cfg.B, cfg.S, cfg.Hq, cfg.D), gen, device, _DT[cfg.dtype])
+
+
 def make_decode_inputs(cfg: Config, seed: int = 0, device="cpu"):
     """Decode inputs: X [B,1,dm], W, Q [B,1,Hq,D], K,V cache [B,L,Hkv,D]."""
     assert cfg.decode

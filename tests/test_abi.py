@@ -120,6 +120,60 @@ def test_decode_split_arithmetic(lib):
     assert lib.gsa_decode_workspace_bytes(2, 10, 4, 3, 128, 0) == 0
 
 
+def bwd(lib, X=FAKE, W=FAKE, G=FAKE, Q=FAKE, LSE=FAKE, dX=FAKE, dW=FAKE, dQ=FAKE, B=1, S=8, Hq=8, Hkv=2,
+        D=128, dm=64, mode=1, dtype=1, ws=FAKE, wsb=1 << 30):
+    return lib.gsa_backward(X, W, G, Q, FAKE, FAKE, FAKE, LSE, FAKE, dX, dW, dQ, FAKE, FAKE,
+                            B, S, Hq, Hkv, D, dm, mode, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(LSE=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(dQ=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(X=None), _lib.GSA_ERR_INVALID_ARG),          # gate without X
+    (dict(dW=None), _lib.GSA_ERR_INVALID_ARG),
+    (dict(G=None, mode=0), _lib.GSA_ERR_INVALID_ARG),  # no gate but X, W, dX, dW given
+    (dict(Hkv=3), _lib.GSA_ERR_INVALID_ARG),
+    (dict(dm=0), _lib.GSA_ERR_INVALID_ARG),
+    (dict(dtype=0), _lib.GSA_ERR_UNSUPPORTED),         # fp32 backward
+    (dict(D=96), _lib.GSA_ERR_UNSUPPORTED),
+    (dict(dm=60), _lib.GSA_ERR_UNSUPPORTED),
+    (dict(Hq=4, Hkv=4, mode=2), _lib.GSA_ERR_UNSUPPORTED),   # headwise gate width 4
+    (dict(dX=MIS), _lib.GSA_ERR_MISALIGNED),
+    (dict(ws=MIS), _lib.GSA_ERR_MISALIGNED),
+    (dict(LSE=FAKE + 2), _lib.GSA_ERR_MISALIGNED),
+    (dict(wsb=16), _lib.GSA_ERR_WORKSPACE),
+    (dict(ws=None), _lib.GSA_ERR_WORKSPACE),
+])
+def test_backward_argument_checks(lib, kw, code):
+    assert bwd(lib, **kw) == code
+    assert lib.gsa_last_error_message().decode().startswith("gsa_backward")
+
+
+@pytest.mark.skipif("have_gpu()", reason="a GPU is visible: valid-looking fake pointers must not be launched")
+def test_backward_no_gate_takes_no_gate_tensors(lib):
+    st = lib.gsa_backward(None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                          FAKE, 1, 8, 8, 2, 128, 0, 0, 1, FAKE, 1 << 30, None)
+    assert st == _lib.GSA_ERR_NO_DEVICE
+
+
+def test_backward_workspace_arithmetic(lib):
+    al = lambda x: -(-x // 256) * 256
+    B, S, Hq, Hkv, D = 2, 100, 8, 2, 64
+    # no gate: only the per-row D values
+    assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 0) == al(B * Hq * S * 4)
+    # gate: dY (bf16), D values, dZ (bf16), then dW partials
+    for mode, N, dm in [(1, Hq * D, 64), (2, Hq, 4096)]:
+        got = lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, dm, mode)
+        base = al(B * S * Hq * D * 2) + al(B * Hq * S * 4) + al(B * S * N * 2)
+        extra = got - base          # 0, or the 256-aligned partial sums of k > 1 token chunks
+        assert extra == 0 or any(extra == al(k * dm * N * 4) for k in range(2, 1025)), extra
+    assert lib.gsa_backward_workspace_bytes(0, S, Hq, Hkv, D, 64, 1) == 0
+    assert lib.gsa_backward_workspace_bytes(B, S, Hq, 3, D, 64, 1) == 0
+    assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 1) == 0
+    assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 64, 9) == 0
+
+
 @pytest.mark.skipif("have_gpu()", reason="a GPU is visible: valid-looking fake pointers must not be launched")
 def test_valid_arguments_without_a_gpu_report_no_device(lib):
     assert fwd(lib) == _lib.GSA_ERR_NO_DEVICE

@@ -1,0 +1,166 @@
+"""Backward of the gated path on the GPU (forward LSE output, gsa_backward)
+against the fp64 oracle on the same bf16 inputs, plus bit-exact causality."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_softmax_attention_amd as gsa
+from synth import CONFIGS, make_inputs, make_grad
+from helpers import TOL, f64, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def small_cfg(B, S, Hq, Hkv, D, mode, dtype="bf16", dm=64):
+    return CONFIGS["tiny_fp32"].with_(name="t", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, mode=mode,
+                                      dtype=dtype, d_model=dm)
+
+
+# --------------------------------------------------------------- LSE from the forward
+LSE_TOL = {"fp32": 1e-4, "bf16": 4e-3}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,mode", [
+    (1, 1, 2, 1, 128, "elementwise"), (2, 129, 4, 2, 128, "headwise"), (1, 300, 8, 8, 64, "elementwise"),
+    (1, 200, 16, 2, 128, "none"), (1, 511, 2, 2, 64, "headwise")])
+def test_forward_lse(B, S, Hq, Hkv, D, mode, dtype):
+    cfg = small_cfg(B, S, Hq, Hkv, D, mode, dtype)
+    inp = make_inputs(cfg, seed=S + 11 * Hq, device=DEV)
+    G = None if mode == "none" else gsa.gate_logits(inp["X"], inp["W"])
+    Y0 = gsa.forward(inp["Q"], inp["K"], inp["V"], G, mode)
+    Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16) if Y0.dtype == torch.bfloat16 else Y0,
+                       Y.view(torch.int16) if Y.dtype == torch.bfloat16 else Y), "forward_lse changed Y"
+    _, lse = oracle.sdpa(f64(inp["Q"]), f64(inp["K"]), f64(inp["V"]), return_lse=True)
+    report(LSE.cpu().numpy(), lse, LSE_TOL[dtype], f"LSE {dtype} B{B} S{S} {Hq}/{Hkv} D{D}")
+
+
+# --------------------------------------------------------------- gsa_backward vs the oracle
+def bwd_tol(ref):
+    """The bf16 bar (2e-2 max-abs) scaled by the gradient's RMS when that exceeds 1:
+    every bf16 rounding on the way (g·dY', P, dS, dZ and the output) is relative."""
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
+    return TOL["bf16"] * max(1.0, rms)
+
+
+def run_backward(inp, dY, mode):
+    gated = mode != "none"
+    G = gsa.gate_logits(inp["X"], inp["W"]) if gated else None
+    Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, mode)
+    X = inp["X"] if gated else None
+    W = inp["W"] if gated else None
+    out = gsa.backward(X, W, G, inp["Q"], inp["K"], inp["V"], Y, LSE, dY, mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_against_oracle(inp, dY, mode, label):
+    out = run_backward(inp, dY, mode)
+    ref = oracle.gated_sdpa_backward(f64(inp["X"]), f64(inp["W"]), f64(inp["Q"]), f64(inp["K"]),
+                                     f64(inp["V"]), f64(dY), mode)
+    names = ["dQ", "dK", "dV"] + (["dX", "dW"] if mode != "none" else [])
+    for n in names:
+        want = ref[n]
+        got = f64(out[n]).reshape(want.shape)
+        report(got, want, bwd_tol(want), f"{label} {n}")
+        nrm = float(np.linalg.norm(want))
+        if nrm > 0:   # (a single key makes dQ exactly zero: then only the max-abs bar applies)
+            rel = float(np.linalg.norm(got - want)) / nrm
+            print(f"  {label} {n}: rms_ref={np.sqrt(np.mean(want ** 2)):.3e} rel_fro={rel:.3e}", flush=True)
+            assert rel <= 1e-2, f"{label} {n}: relative Frobenius error {rel:.3e}"
+    if mode == "none":
+        assert out["dX"] is None and out["dW"] is None
+
+
+BWD_CASES = []
+for D in (128, 64):
+    for (B, S, Hq, Hkv, mode) in [(1, 1, 8, 1, "elementwise"), (2, 7, 8, 8, "headwise"),
+                                  (1, 64, 2, 2, "elementwise"), (1, 65, 8, 1, "headwise"),
+                                  (2, 129, 4, 2, "elementwise"), (1, 200, 16, 2, "headwise"),
+                                  (1, 300, 8, 8, "elementwise"), (1, 257, 4, 2, "none")]:
+        BWD_CASES.append((B, S, Hq, Hkv, D, mode))
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,mode", BWD_CASES)
+def test_backward_small_shapes(B, S, Hq, Hkv, D, mode):
+    cfg = small_cfg(B, S, Hq, Hkv, D, mode)
+    seed = 5 * S + Hq + D
+    inp = make_inputs(cfg, seed=seed, device=DEV)
+    dY = make_grad(cfg, seed=seed, device=DEV)
+    check_against_oracle(inp, dY, mode, f"B{B} S{S} {Hq}/{Hkv} D{D} {mode}")
+
+
+@pytest.mark.parametrize("dm,mode", [(200, "elementwise"), (136, "headwise"), (1024, "elementwise")])
+def test_backward_gate_widths(dm, mode):
+    """d_model and token counts that are not multiples of the 128-wide GEMM tiles."""
+    cfg = small_cfg(1, 333, 8, 2, 64, mode, dm=dm)
+    inp = make_inputs(cfg, seed=dm, device=DEV)
+    dY = make_grad(cfg, seed=dm, device=DEV)
+    check_against_oracle(inp, dY, mode, f"dm{dm} {mode}")
+
+
+def test_backward_rejects_unsupported():
+    cfg = small_cfg(1, 16, 4, 4, 64, "headwise")          # headwise gate width 4: not a multiple of 8
+    inp = make_inputs(cfg, seed=1, device=DEV)
+    dY = make_grad(cfg, seed=1, device=DEV)
+    G = gsa.gate_logits(inp["X"], inp["W"])
+    Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, "headwise")
+    with pytest.raises(gsa.GsaError, match="multiples of 8"):
+        gsa.backward(inp["X"], inp["W"], G, inp["Q"], inp["K"], inp["V"], Y, LSE, dY, "headwise")
+    cfg32 = small_cfg(1, 16, 2, 2, 64, "none", dtype="fp32")
+    i32 = make_inputs(cfg32, seed=1, device=DEV)
+    Y32, L32 = gsa.forward_lse(i32["Q"], i32["K"], i32["V"], None, "none")
+    with pytest.raises(gsa.GsaError, match="BF16"):
+        gsa.backward(None, None, None, i32["Q"], i32["K"], i32["V"], Y32, L32, Y32, "none")
+
+
+# --------------------------------------------------------------- bit-exact causality
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu()
+
+
+def _redraw(t, gen):
+    """Seeded N(0,1) values of t's shape and dtype."""
+    return torch.randn(tuple(t.shape), generator=gen, device=t.device, dtype=torch.float32).to(t.dtype)
+
+
+@pytest.mark.parametrize("mode", ["elementwise", "headwise"])
+def test_backward_causality_bitwise(mode):
+    """dQ of rows <= c ignores every token after c; dK, dV of keys > c ignore every
+    query row <= c (Q, dY and X of those rows), bit for bit."""
+    cfg = small_cfg(2, 300, 8, 2, 128, mode)
+    inp = make_inputs(cfg, seed=77, device=DEV)
+    dY = make_grad(cfg, seed=77, device=DEV)
+    base = run_backward(inp, dY, mode)
+    c = 130
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(78)
+    fut = {k: v.clone() for k, v in inp.items()}
+    for k in ("Q", "K", "V", "X"):
+        fut[k][:, c + 1:] = _redraw(fut[k][:, c + 1:], gen)
+    dYf = dY.clone()
+    dYf[:, c + 1:] = -dYf[:, c + 1:]
+    a = run_backward(fut, dYf, mode)
+    assert torch.equal(_bits(base["dQ"][:, :c + 1]), _bits(a["dQ"][:, :c + 1]))
+    past = {k: v.clone() for k, v in inp.items()}
+    past["Q"][:, :c + 1] = _redraw(past["Q"][:, :c + 1], gen)
+    dYp = dY.clone()
+    dYp[:, :c + 1] = 2 * dYp[:, :c + 1]
+    p = run_backward(past, dYp, mode)
+    for n in ("dK", "dV"):
+        assert torch.equal(_bits(base[n][:, c + 1:]), _bits(p[n][:, c + 1:])), n
+
+
+def test_backward_is_deterministic():
+    cfg = small_cfg(1, 257, 8, 2, 128, "elementwise", dm=256)
+    inp = make_inputs(cfg, seed=9, device=DEV)
+    dY = make_grad(cfg, seed=9, device=DEV)
+    a = run_backward(inp, dY, "elementwise")
+    b = run_backward(inp, dY, "elementwise")
+    for n in ("dQ", "dK", "dV", "dX"):
+        assert torch.equal(_bits(a[n]), _bits(b[n])), n
+    assert torch.equal(a["dW"].cpu(), b["dW"].cpu())
