@@ -2,6 +2,7 @@
 // The declarations and their contracts are in include/gsa.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -24,8 +25,10 @@ int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv);
 int64_t decode_chunk(int64_t L, int64_t nsplit);
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
                            const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
-                           float* Dv, void* dZ, int B, int S, int Hq, int Hkv, int D, int mode,
-                           hipStream_t stream);
+                           float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
+                           int mode, hipStream_t stream);
+int bwd_kv_slices(int B, int S, int Hq, int Hkv);
+int bwd_stat_rows(int S);
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
                               int64_t N, hipStream_t st);
 hipError_t launch_bwd_gemm_dw(const void* X, const void* dZ, float* dW, float* partials, int64_t M,
@@ -247,31 +250,39 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
 
 namespace {
 // Workspace of gsa_backward, each region 256-byte aligned:
-//   dY  = dY' ⊙ g      bf16 [B, S, Hq, D]   (gated modes)
-//   Dv  = Σ_d dY'·Y'   fp32 [B, Hq, S]
-//   dZ                 bf16 [B*S, N]        (gated modes)
-//   dW_θ partials      fp32 [splits, d_model, N]  (gated modes, splits > 1)
+//   dY  = dY' ⊙ g                 bf16 [B, S, Hq, D]          (gated modes)
+//   per-row statistics            fp32 2 x [B*Hq, Sp]          (base-2 LSE, then D; Sp = S rounded up to 64)
+//   dZ                            bf16 [B*S, N]                (gated modes)
+//   partial sums                  fp32, the larger of
+//       dK, dV slices             2 x [slices, B, S, Hkv, D]   (when a GQA group is split)
+//       dW_θ token chunks         [splits, d_model, N]         (gated modes, splits > 1)
+//   (both partial sets are consumed before the next kernel on the stream starts,
+//   so they share one region)
 struct BwdLayout {
-  size_t dy = 0, dv = 0, dz = 0, part = 0, total = 0;
+  size_t dy = 0, stat = 0, dz = 0, part = 0, total = 0;
   int64_t splits = 1;
 };
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-BwdLayout bwd_layout(int64_t B, int64_t S, int64_t Hq, int64_t D, int64_t d_model, int mode) {
+BwdLayout bwd_layout(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model, int mode) {
   BwdLayout l;
   const bool gated = mode != GSA_GATE_NONE;
   const int64_t M = B * S, N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
   size_t off = 0;
   l.dy = off;
   if (gated) off += align256((size_t)(M * Hq * D) * 2);
-  l.dv = off;
-  off += align256((size_t)(B * Hq * S) * 4);
+  l.stat = off;
+  off += align256((size_t)(2 * B * Hq * gsa::bwd_stat_rows((int)S)) * 4);
   l.dz = off;
   if (gated) off += align256((size_t)(M * N) * 2);
   l.part = off;
+  size_t part = 0;
+  const int64_t ns = gsa::bwd_kv_slices((int)B, (int)S, (int)Hq, (int)Hkv);
+  if (ns > 1) part = (size_t)(2 * ns * M * Hkv * D) * 4;
   if (gated) {
     l.splits = gsa::bwd_dw_splits(M, d_model, N);
-    if (l.splits > 1) off += align256((size_t)(l.splits * d_model * N) * 4);
+    if (l.splits > 1) part = std::max(part, (size_t)(l.splits * d_model * N) * 4);
   }
+  off += align256(part);
   l.total = off;
   return l;
 }
@@ -284,7 +295,7 @@ size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hk
   if (mode != GSA_GATE_NONE && mode != GSA_GATE_ELEMENTWISE && mode != GSA_GATE_HEADWISE) return 0;
   if (mode != GSA_GATE_NONE && d_model <= 0) return 0;
   if (B * S > kIntMax || Hq > 4096 || D > 128 || d_model > kIntMax) return 0;
-  return bwd_layout(B, S, Hq, D, d_model, mode).total;
+  return bwd_layout(B, S, Hq, Hkv, D, d_model, mode).total;
 }
 
 gsa_status gsa_backward(const void* X, const void* W, const float* G, const void* Q, const void* K,
@@ -316,7 +327,7 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
     if (p && !aligned16(p))
       return fail(GSA_ERR_MISALIGNED, "%s: every tensor and the workspace must be 16-byte aligned", fn);
   if (((uintptr_t)LSE % 4) != 0) return fail(GSA_ERR_MISALIGNED, "%s: LSE must be 4-byte aligned", fn);
-  const BwdLayout lay = bwd_layout(B, S, Hq, D, d_model, mode);
+  const BwdLayout lay = bwd_layout(B, S, Hq, Hkv, D, d_model, mode);
   if (workspace == nullptr || workspace_bytes < lay.total)
     return fail(GSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -325,8 +336,8 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
   hipStream_t st = (hipStream_t)stream;
   void* dz = gated ? ws + lay.dz : nullptr;
   hipError_t e = gsa::launch_attn_bwd(Q, K, V, dY, Y, G, LSE, dQ, dK, dV, gated ? ws + lay.dy : nullptr,
-                                      (float*)(ws + lay.dv), dz, (int)B, (int)S, (int)Hq, (int)Hkv, (int)D,
-                                      mode, st);
+                                      (float*)(ws + lay.stat), dz, (float*)(ws + lay.part), (int)B, (int)S,
+                                      (int)Hq, (int)Hkv, (int)D, mode, st);
   if (e != hipSuccess) return hip_result(e, "gsa_backward attention launch");
   if (gated) {
     e = gsa::launch_bwd_gemm_dx(dz, W, dX, M, d_model, N, st);

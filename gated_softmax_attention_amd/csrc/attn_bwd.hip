@@ -41,12 +41,16 @@ constexpr uint32_t kOOB = 0xfffffff0u;
 enum : int { kBwdGateNone = 0, kBwdGateElem = 1, kBwdGateHead = 2 };
 
 // ---------------------------------------------------------------- prep
-// One (token, head) row per 16 threads, 8 head dims per thread.
+// One (token, head) row per D/8 threads, 8 head dims per thread.  Besides dY
+// and dZ it writes the per-row statistics both attention kernels read: Stat
+// holds [B*Hq][Sp] base-2 LSE values, then [B*Hq][Sp] D values (Sp = S rounded
+// up to 64; the padding rows hold zeros and are always masked).
 template <int D, int MODE>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const bf16* __restrict__ dYg, const bf16* __restrict__ Yg,
-                     const float* __restrict__ Gate, bf16* __restrict__ dY, float* __restrict__ Dv,
-                     bf16* __restrict__ dZ, int B, int S, int Hq) {
+                     const float* __restrict__ Gate, const float* __restrict__ Lse,
+                     bf16* __restrict__ dY, float* __restrict__ Stat, bf16* __restrict__ dZ, int B, int S,
+                     int Hq, int Sp) {
   constexpr int TPR = D / 8;                 // threads per row
   constexpr int RPB = 256 / TPR;             // rows per block
   const int tid = threadIdx.x;
@@ -101,7 +105,14 @@ void bwd_prep_kernel(const bf16* __restrict__ dYg, const bf16* __restrict__ Yg,
   }
   if (part == 0) {
     const int64_t b = tok / S, i = tok % S;
-    Dv[(b * Hq + head) * S + i] = dsum;
+    const int64_t bh = b * Hq + head;
+    Stat[bh * Sp + i] = Lse[bh * S + i] * kLog2e;
+    Stat[((int64_t)B * Hq + bh) * Sp + i] = dsum;
+    if (i == S - 1)
+      for (int64_t j = S; j < Sp; ++j) {
+        Stat[bh * Sp + j] = 0.f;
+        Stat[((int64_t)B * Hq + bh) * Sp + j] = 0.f;
+      }
     if constexpr (MODE == kBwdGateHead) dZ[tok * Hq + head] = (bf16)((1.0f - g[0]) * dsum);
   }
 }
@@ -196,9 +207,9 @@ __device__ __forceinline__ void pack_b(const f32x16 (&s)[2], bf16x8 (&pb)[2][2])
 template <int D>
 __global__ __launch_bounds__(256, 1)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                   const bf16* __restrict__ dY, const float* __restrict__ Lse,
-                   const float* __restrict__ Dv, bf16* __restrict__ dQ, int B, int S, int Hq,
-                   int Hkv, int n_qtiles, float scale) {
+                   const bf16* __restrict__ dY, const float* __restrict__ Stat,
+                   bf16* __restrict__ dQ, int B, int S, int Hq, int Hkv, int n_qtiles, int Sp,
+                   float scale) {
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
   __shared__ __align__(16) char Ks[2][KT * RSB];
@@ -231,8 +242,12 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     }
   }
   const int qc = min(my_q, S - 1);
-  const float lse2 = Lse[((int64_t)b * Hq + head) * S + qc] * kLog2e;
-  const float dval = Dv[((int64_t)b * Hq + head) * S + qc];
+  float lse2 = Stat[((int64_t)b * Hq + head) * Sp + qc];
+  float dval = Stat[((int64_t)(B + b) * Hq + head) * Sp + qc];
+  // settle these loads before the loop (see the dK/dV kernel)
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]), "+v"(yf[kk]));
+  asm volatile("" : "+v"(lse2), "+v"(dval));
 
   const uint32_t row_b = (uint32_t)(kv_row * 2);
   const uint32_t kv_bytes = (uint32_t)(((int64_t)S * kv_row - (int64_t)kvh * D) * 2);
@@ -285,15 +300,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
         s[sub] = mfma32x32x16(row_read<D>(kt, sub * 32 + l32, kk, hl), qf[kk], s[sub]);
         dp[sub] = mfma32x32x16(row_read<D>(vt, sub * 32 + l32, kk, hl), yf[kk], dp[sub]);
       }
-    // element (sub, r) is key k0 + sub*32 + 8*(r/4) + 4*hl + r%4 of query my_q
-    const bool masked = (k0 + KT - 1 > qw0) || (k0 + KT > S);
+    // element (sub, r) is key k0 + sub*32 + 8*(r/4) + 4*hl + r%4 of query my_q;
+    // only tiles reaching past the wave's first query need the causal mask
+    // (keys past S hold zeros and only ever meet masked or discarded rows)
+    if (k0 + KT - 1 > qw0) {
+      const int lim = qc - k0 - 4 * hl;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (sub * 32 + 8 * (r >> 2) + (r & 3) > lim) s[sub][r] = -INFINITY;
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool vis = !masked || (key <= qc && key < S);
-        const float p = vis ? fast_exp2(fmaf(s[sub][r], scale_log2, -lse2)) : 0.f;
+        const float p = fast_exp2(fmaf(s[sub][r], scale_log2, -lse2));
         s[sub][r] = p * (dp[sub][r] - dval);   // dS
       }
     bf16x8 ds[2][2];
@@ -321,28 +343,35 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
 // ---------------------------------------------------------------- dK, dV
 // 256 threads: 128 keys of one key/value head (4 waves x 32).  For each query
-// head of the group and each 64-row query tile that sees these keys:
+// head of the workgroup's slice of the group and each 64-row query tile that
+// sees these keys:
 //   S = Q·Kᵀ, dP = dY·Vᵀ      (A = Q / dY rows from LDS, B = K / V fragments)
 //   dVᵀ += dYᵀ·P, dKᵀ += Qᵀ·dS (A through transposed reads, B = P / dS in bf16)
-template <int D>
+// The query heads of a group may be cut into `nsplit` slices (one workgroup
+// each) so small-Hkv shapes still fill the chip; slices then write float32
+// partial sums [nsplit][B][S][Hkv][D] that bwd_sum_slices adds in order.
+template <int D, bool PARTIAL>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                     const bf16* __restrict__ dY, const float* __restrict__ Lse,
-                     const float* __restrict__ Dv, bf16* __restrict__ dK, bf16* __restrict__ dV,
-                     int B, int S, int Hq, int Hkv, int n_ktiles, float scale) {
+                     const bf16* __restrict__ dY, const float* __restrict__ Stat,
+                     bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKp,
+                     float* __restrict__ dVp, int B, int S, int Hq, int Hkv, int Sp, int nsplit,
+                     float scale) {
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
   __shared__ __align__(16) char Qs[2][QW * RSB];
   __shared__ __align__(16) char Ys[2][QW * RSB];
+  __shared__ __align__(16) float Ss[2][256];   // per stage: base-2 LSE of 64 rows, D of 64 rows, pad
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int bid = blockIdx.x;
-  const int hb = Hkv * B;
-  const int kt_i = bid / hb;                       // light (early) key tiles have the most work: first
-  const int pair = bid % hb;
+  const int hb = Hkv * B * nsplit;
+  const int kt_i = bid / hb;                       // early key tiles see the most queries: first
+  const int rest = bid % hb;
+  const int slice = rest % nsplit, pair = rest / nsplit;
   const int kvh = pair % Hkv, b = pair / Hkv;
-  const int G = Hq / Hkv;
+  const int G = Hq / Hkv, Gs = G / nsplit;
   const int k0 = kt_i * KW, kw0 = k0 + wave * 32, my_k = kw0 + l32;
   const int64_t q_row = (int64_t)Hq * D, kv_row = (int64_t)Hkv * D;
   const float scale_log2 = scale * kLog2e;
@@ -359,16 +388,24 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       kf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(kr, o + 32 * kk, 0));
       vf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(vr, o + 32 * kk, 0));
     }
+    // settle these loads here: otherwise the compiler re-waits for them inside
+    // the loop, and that wait also drains the next tile's direct loads
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
   }
   const uint32_t row_b = (uint32_t)(q_row * 2);
   TileLoader<D, QW> ld;
   ld.init(wave, lane, row_b);
-  uint32_t qs_lds[2], ys_lds[2];
+  uint32_t qs_lds[2], ys_lds[2], st_lds[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     qs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Qs[i][0]));
     ys_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ys[i][0]));
+    st_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ss[i][0]));
   }
+  // statistics loads (wave 0): lanes 0..15 take 4 LSE rows each, lanes 16..31 4 D rows
+  const auto srs = make_rsrc(Stat, (uint32_t)((int64_t)2 * B * Hq * Sp * 4));
+  const uint32_t st_lane = lane < 16 ? 16u * lane : (uint32_t)((int64_t)B * Hq * Sp * 4) + 16u * (lane - 16);
   uint32_t trb[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
@@ -385,9 +422,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // query tiles that see keys [k0, k0 + KW): rows >= k0
   const int qt_first = k0 / QW;
   const int n_qt = ceil_div(S, QW) - qt_first;
-  const int n_steps = G * max(n_qt, 0);
+  const int n_steps = Gs * max(n_qt, 0);
+  const int head0 = kvh * G + slice * Gs;
   auto tile_of = [&](int step, int& head, int& qs0) {
-    head = kvh * G + step / n_qt;
+    head = head0 + step / n_qt;
     qs0 = (qt_first + step % n_qt) * QW;
   };
   auto issue = [&](int step, int buf) {
@@ -398,32 +436,21 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     const auto yr = make_rsrc(dY + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
     ld.load(qr, row_b, qs0, S, qs_lds[buf], wave);
     ld.load(yr, row_b, qs0, S, ys_lds[buf], wave);
+    if (wave == 0)
+      dma16_lds(srs, lane < 32 ? st_lane + (uint32_t)(((int64_t)b * Hq + head) * Sp + qs0) * 4u : kOOB,
+                st_lds[buf]);
   };
   if (n_steps > 0) issue(0, 0);
   for (int step = 0; step < n_steps; ++step) {
     const int buf = step & 1;
     int head, qs0;
     tile_of(step, head, qs0);
-    // LSE (base 2) and D of the 2x16 query rows this lane's registers hold:
-    // row qs0 + 32*sub + 8*(r/4) + 4*hl + r%4
-    float lse2[2][16], dval[2][16];
-    {
-      const float* lrow = Lse + ((int64_t)b * Hq + head) * S;
-      const float* drow = Dv + ((int64_t)b * Hq + head) * S;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = min(qs0 + 32 * sub + 8 * (r >> 2) + 4 * hl + (r & 3), S - 1);
-          lse2[sub][r] = lrow[qrow] * kLog2e;
-          dval[sub][r] = drow[qrow];
-        }
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (step + 1 < n_steps) issue(step + 1, buf ^ 1);
     const GSA_LDS_B char* qt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Qs[buf][0];
     const GSA_LDS_B char* yt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ys[buf][0];
+    const GSA_LDS_B float* st = (const GSA_LDS_B float*)(GSA_LDS_B void*)&Ss[buf][0];
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -439,21 +466,37 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
         s[sub] = mfma32x32x16(row_read<D>(qt, sub * 32 + l32, kk, hl), kf[kk], s[sub]);
         dp[sub] = mfma32x32x16(row_read<D>(yt, sub * 32 + l32, kk, hl), vf[kk], dp[sub]);
       }
-    // element (sub, r): query qs0 + 32*sub + 8*(r/4) + 4*hl + r%4, key my_k
-    f32x16 ds[2];
+    // element (sub, r): query qs0 + 32*sub + 8*(r/4) + 4*hl + r%4, key my_k.
+    // A wave needs the mask only where its keys pass the tile's first query or
+    // the tile runs past S (rows past S hold zero statistics and must not count).
+    if ((qs0 < kw0 + 31) || (qs0 + QW > S)) {
+      const int lo = my_k - qs0 - 4 * hl, hi = S - 1 - qs0 - 4 * hl;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * sub + 8 * (r >> 2) + (r & 3);
+          if (off < lo || off > hi) s[sub][r] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = qs0 + 32 * sub + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool vis = my_k <= qrow && qrow < S && my_k < S;
-        const float p = vis ? fast_exp2(fmaf(s[sub][r], scale_log2, -lse2[sub][r])) : 0.f;
-        ds[sub][r] = p * (dp[sub][r] - dval[sub][r]);
-        s[sub][r] = p;
+      for (int i = 0; i < 4; ++i) {
+        const int row4 = 32 * sub + 8 * i + 4 * hl;
+        const f32x4 l4 = *(const GSA_LDS_B f32x4*)(st + row4);
+        const f32x4 d4 = *(const GSA_LDS_B f32x4*)(st + 64 + row4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          const float p = fast_exp2(fmaf(s[sub][r], scale_log2, -l4[j]));
+          dp[sub][r] = p * (dp[sub][r] - d4[j]);   // dS
+          s[sub][r] = p;
+        }
       }
     bf16x8 pb[2][2], db[2][2];
     pack_b(s, pb);
-    pack_b(ds, db);
+    pack_b(dp, db);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -467,60 +510,110 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   }
 
   if (my_k >= S) return;
-  bf16* ok = dK + ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
-  bf16* ov = dV + ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
+  const int64_t orow = ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = dt * 32 + 8 * i + 4 * hl;
-      *(u32x2*)(ok + d0) = u32x2{pack_bf16x2(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale),
-                                 pack_bf16x2(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale)};
-      *(u32x2*)(ov + d0) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
-                                 pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+      if constexpr (PARTIAL) {
+        const int64_t o = (int64_t)slice * B * S * kv_row + orow + d0;
+        *(f32x4*)(dKp + o) = f32x4{dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale,
+                                   dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale};
+        *(f32x4*)(dVp + o) = f32x4{dv[dt][4 * i], dv[dt][4 * i + 1], dv[dt][4 * i + 2], dv[dt][4 * i + 3]};
+      } else {
+        *(u32x2*)(dK + orow + d0) = u32x2{pack_bf16x2(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale),
+                                          pack_bf16x2(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale)};
+        *(u32x2*)(dV + orow + d0) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
+                                          pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+      }
     }
 }
 
+// dK, dV (bf16) = Σ over slices of the float32 partial sums, in slice order;
+// 4 elements per thread (n4 = element count / 4).
+__global__ __launch_bounds__(256)
+void bwd_sum_slices_kernel(const f32x4* __restrict__ dKp, const f32x4* __restrict__ dVp, u32x2* __restrict__ dK,
+                           u32x2* __restrict__ dV, int64_t n4, int nsplit) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 a = dKp[i], c = dVp[i];
+    for (int z = 1; z < nsplit; ++z) {
+      a += dKp[(int64_t)z * n4 + i];
+      c += dVp[(int64_t)z * n4 + i];
+    }
+    dK[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    dV[i] = u32x2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+  }
+}
+
 // ---------------------------------------------------------------- launch
+// Query-head slices per key/value head for the dK/dV kernel: the smallest
+// divisor of the group size that gives about 1024 workgroups.
+int bwd_kv_slices(int B, int S, int Hq, int Hkv) {
+  const int G = Hq / Hkv;
+  const int64_t base = (int64_t)ceil_div(S, bwd::KW) * Hkv * B;
+  for (int ns = 1; ns < G; ++ns)
+    if (G % ns == 0 && base * ns >= 1024) return ns;
+  return G;
+}
+int bwd_stat_rows(int S) { return ceil_div(S, 64) * 64; }
+
 template <int D>
 static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* dYg,
                                const void* Yg, const float* G, const float* Lse, void* dQ, void* dK,
-                               void* dV, void* dY, float* Dv, void* dZ, int B, int S, int Hq, int Hkv,
-                               int mode, hipStream_t st) {
+                               void* dV, void* dY, float* Stat, void* dZ, float* part, int B, int S,
+                               int Hq, int Hkv, int mode, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)D);
+  const int Sp = bwd_stat_rows(S);
   const int64_t rows = (int64_t)B * S * Hq;
   const int rpb = 256 / (D / 8);
   const unsigned pblocks = (unsigned)((rows + rpb - 1) / rpb);
   const bf16* dy_attn = (const bf16*)dY;
   if (mode == kBwdGateElem)
     hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateElem>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
-                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+                       (const bf16*)Yg, G, Lse, (bf16*)dY, Stat, (bf16*)dZ, B, S, Hq, Sp);
   else if (mode == kBwdGateHead)
     hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateHead>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
-                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+                       (const bf16*)Yg, G, Lse, (bf16*)dY, Stat, (bf16*)dZ, B, S, Hq, Sp);
   else {
     hipLaunchKernelGGL((bwd_prep_kernel<D, kBwdGateNone>), dim3(pblocks), dim3(256), 0, st, (const bf16*)dYg,
-                       (const bf16*)Yg, G, (bf16*)dY, Dv, (bf16*)dZ, B, S, Hq);
+                       (const bf16*)Yg, G, Lse, (bf16*)dY, Stat, (bf16*)dZ, B, S, Hq, Sp);
     dy_attn = (const bf16*)dYg;   // no gate: the SDPA output's gradient is dY' itself
   }
   const int nq = ceil_div(S, bwd::QT);
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((int64_t)nq * Hq * B)), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, Lse, (const float*)Dv,
-                     (bf16*)dQ, B, S, Hq, Hkv, nq, scale);
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, (bf16*)dQ,
+                     B, S, Hq, Hkv, nq, Sp, scale);
   const int nk = ceil_div(S, bwd::KW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)((int64_t)nk * Hkv * B)), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, Lse, (const float*)Dv,
-                     (bf16*)dK, (bf16*)dV, B, S, Hq, Hkv, nk, scale);
+  const int ns = bwd_kv_slices(B, S, Hq, Hkv);
+  const unsigned grid = (unsigned)((int64_t)nk * Hkv * B * ns);
+  if (ns == 1) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
+                       (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, (bf16*)dK, (bf16*)dV,
+                       nullptr, nullptr, B, S, Hq, Hkv, Sp, 1, scale);
+  } else {
+    const int64_t n = (int64_t)B * S * Hkv * D;
+    float* dKp = part;
+    float* dVp = part + ns * n;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
+                       (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, nullptr, nullptr, dKp,
+                       dVp, B, S, Hq, Hkv, Sp, ns, scale);
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div<int64_t>(n / 4, 256), 4096);
+    hipLaunchKernelGGL(bwd_sum_slices_kernel, dim3(blocks), dim3(256), 0, st, (const f32x4*)dKp,
+                       (const f32x4*)dVp, (u32x2*)dK, (u32x2*)dV, n / 4, ns);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
                            const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
-                           float* Dv, void* dZ, int B, int S, int Hq, int Hkv, int D, int mode,
-                           hipStream_t stream) {
+                           float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
+                           int mode, hipStream_t stream) {
   if (D == 128)
-    return launch_bwd_d<128>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Dv, dZ, B, S, Hq, Hkv, mode, stream);
-  return launch_bwd_d<64>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Dv, dZ, B, S, Hq, Hkv, mode, stream);
+    return launch_bwd_d<128>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Stat, dZ, part, B, S, Hq, Hkv, mode,
+                             stream);
+  return launch_bwd_d<64>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Stat, dZ, part, B, S, Hq, Hkv, mode,
+                          stream);
 }
 
 }  // namespace gsa

@@ -159,15 +159,20 @@ def test_backward_no_gate_takes_no_gate_tensors(lib):
 
 def test_backward_workspace_arithmetic(lib):
     al = lambda x: -(-x // 256) * 256
-    B, S, Hq, Hkv, D = 2, 100, 8, 2, 64
-    # no gate: only the per-row D values
-    assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 0) == al(B * Hq * S * 4)
-    # gate: dY (bf16), D values, dZ (bf16), then dW partials
+    B, S, Hq, Hkv, D = 2, 100, 8, 8, 64      # Hkv == Hq: no split GQA groups
+    Sp = 128                                 # rows of the statistics: S rounded up to 64
+    # no gate: only the per-row statistics (base-2 LSE and D)
+    assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 0) == al(2 * B * Hq * Sp * 4)
+    # gate: dY (bf16), statistics, dZ (bf16), then dW partials
     for mode, N, dm in [(1, Hq * D, 64), (2, Hq, 4096)]:
         got = lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, dm, mode)
-        base = al(B * S * Hq * D * 2) + al(B * Hq * S * 4) + al(B * S * N * 2)
+        base = al(B * S * Hq * D * 2) + al(2 * B * Hq * Sp * 4) + al(B * S * N * 2)
         extra = got - base          # 0, or the 256-aligned partial sums of k > 1 token chunks
         assert extra == 0 or any(extra == al(k * dm * N * 4) for k in range(2, 1025)), extra
+    # a GQA group split across workgroups adds float32 partial dK and dV
+    stat1 = al(2 * 8 * Sp * 4)
+    ws1 = lib.gsa_backward_workspace_bytes(1, 100, 8, 1, 64, 0, 0)
+    assert ws1 > stat1 and (ws1 - stat1) % (2 * 100 * 64 * 4) == 0
     assert lib.gsa_backward_workspace_bytes(0, S, Hq, Hkv, D, 64, 1) == 0
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, 3, D, 64, 1) == 0
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 1) == 0
