@@ -8,8 +8,9 @@ SDPA).  Inputs are seeded synthetic tensors already resident in HBM.
 Reported (one JSON line): whole-step TFLOP/s; the roofline of the dominant
 kernel (the gated forward), timed per launch with HIP events on the stream it
 runs on; the decode workload (batch 64, one token against a 16384-long KV
-cache, 32/8 heads) as GB/s with its own roofline; and the fp64 oracle timed on
-the host cores on a bounded sample of the prefill workload.
+cache, 32/8 heads) as GB/s with its own roofline; the backward of the prefill
+path (gsa_backward) as TFLOP/s; and the fp64 oracle timed on the host cores on
+a bounded sample of the prefill workload.
 """
 import argparse
 import hashlib
@@ -38,6 +39,7 @@ def parse():
     p.add_argument("--only", choices=["prefill", "decode"], default=None,
                    help="run one workload's GPU part only (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward workload")
     p.add_argument("--no-others", action="store_true",
                    help="skip the gqa_prefill and long_prefill lines (reported beside the headline)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -170,6 +172,44 @@ def decode_bench(args, torch, gsa, cfg):
     }
 
 
+def backward_bench(args, torch, gsa, cfg):
+    """gsa_backward on the prefill workload, from the forward's resident outputs
+    (G, Y', LSE) and a seeded upstream gradient.  The timed unit is the whole
+    call (prep, dQ, dK/dV, dX and dW kernels); its rocprofv3 split is in profiles/."""
+    from synth import make_inputs, make_grad
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    dY = make_grad(cfg, seed=0, device="cuda:0")
+    G = gsa.gate_logits(X, W)
+    Y, LSE = gsa.forward_lse(Q, K, V, G, cfg.mode)
+    ws = torch.empty(gsa.backward_workspace_bytes(cfg.B, cfg.S, cfg.Hq, cfg.Hkv, cfg.D, cfg.d_model,
+                                                  cfg.mode), dtype=torch.uint8, device="cuda:0")
+    holder = {}
+
+    def step():
+        holder["g"] = gsa.backward(X, W, G, Q, K, V, Y, LSE, dY, cfg.mode, workspace=ws)
+
+    ms, _, wall = time_steps(step, step, args.steps, args.warmup, torch)
+    for n in ("dQ", "dK", "dV", "dX", "dW"):
+        if not torch.isfinite(holder["g"][n][:64].float()).all():
+            raise RuntimeError(f"non-finite {n}")
+    flops = cfg.backward_flops()
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": cfg.name, "metric": "gated causal SDPA backward TFLOP/s (% of bf16 MFMA peak)",
+        "value": achieved, "unit": "TFLOP/s", "ms_per_step": ms,
+        "pct_of_peak": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "config": {"B": cfg.B, "S": cfg.S, "d_model": cfg.d_model, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "D": cfg.D, "mode": cfg.mode, "causal": True, "flops_per_step": flops},
+        "roofline": {
+            "kernel": "gsa_backward (prep + dQ + dK/dV + dX + dW kernels)", "bound": "mfma",
+            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "avg_launch_ms": ms,
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+
 def cpu_baseline(args, torch, cfg):
     """The fp64 oracle, as it is, on a bounded sample of the prefill workload:
     every query row r with r % stride == 0 (all batches and heads), with the
@@ -267,6 +307,12 @@ def main():
                    "roofline": dec["roofline"]}
         else:
             out["decode"] = dec
+    if out is not None and not args.no_backward and args.only is None:
+        bwd = backward_bench(args, torch, gsa, pcfg)
+        torch.cuda.empty_cache()
+        print(f"# backward: {bwd['ms_per_step']:.4f} ms/step, {bwd['value']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        out["backward"] = bwd
     if out is not None and not args.no_others and args.only is None:
         # the other prefill workloads, each its own gate GEMM + forward step
         others = {}

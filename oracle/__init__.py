@@ -29,8 +29,9 @@ from .gated_sdpa import (
     gate_scores, sigmoid, gate_values, sdpa, gated_sdpa, gated_decode,
     gate_param_count,
 )
-from .backward import sdpa_backward, gated_sdpa_backward
+from .backward import sdpa_backward, gated_sdpa_backward, gated_sdpa_backward_sampled
 from . import brute
 
 __all__ = ["gate_scores", "sigmoid", "gate_values", "sdpa", "gated_sdpa", "gated_decode",
-           "gate_param_count", "sdpa_backward", "gated_sdpa_backward", "brute"]
+           "gate_param_count", "sdpa_backward", "gated_sdpa_backward",
+           "gated_sdpa_backward_sampled", "brute"]

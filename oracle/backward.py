@@ -91,3 +91,67 @@ def gated_sdpa_backward(X, W, Q, K, V, dYg, mode):
     dW = X.reshape(B * S, -1).T @ dZ.reshape(B * S, -1)
     dQ, dK, dV = sdpa_backward(Q, K, V, dY)
     return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dX, "dW": dW}
+
+
+def gated_sdpa_backward_sampled(X, W, Q, K, V, dYg, mode, kv_heads, rows):
+    """Part of ``gated_sdpa_backward``'s result, for shapes where all of it is too
+    costly: the same chain rule, evaluated only for
+
+      * the key/value heads ``kv_heads``: dK and dV of those heads and dQ of every
+        query head in their groups (all rows);
+      * the dW_θ columns those query heads' gates use (all d_model rows);
+      * the dX rows ``rows`` (every column).
+
+    Returns a dict with q_heads, dQ [B, S, len(q_heads), D], dK and dV
+    [B, S, len(kv_heads), D], w_cols, dW [d_model, len(w_cols)] and dX
+    [B, len(rows), d_model] (the last three None for mode "none"); float64.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dYg = np.asarray(dYg, dtype=np.float64)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    kv_heads = np.asarray(kv_heads, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    q_heads = np.concatenate([np.arange(c * G, (c + 1) * G) for c in kv_heads])
+    gated = mode != "none"
+    per = D if mode == "elementwise" else 1          # gate columns per query head
+    out = {"q_heads": q_heads, "dQ": np.zeros((B, S, len(q_heads), D)),
+           "dK": np.zeros((B, S, len(kv_heads), D)), "dV": np.zeros((B, S, len(kv_heads), D)),
+           "w_cols": None, "dW": None, "dX": None}
+    if gated:
+        X = np.asarray(X, dtype=np.float64)
+        W = np.asarray(W, dtype=np.float64)
+        w_cols = (q_heads[:, None] * per + np.arange(per)[None, :]).ravel()
+        g_cols = sigmoid(gate_scores(X, W[:, w_cols]))   # gates of the sampled heads, every row
+        out["w_cols"] = w_cols
+        out["dW"] = np.zeros((X.shape[-1], len(w_cols)))
+    for i, c in enumerate(kv_heads):
+        hq = slice(c * G, (c + 1) * G)                   # query heads of this group
+        loc = slice(i * G, (i + 1) * G)                  # their place in the output
+        cols = slice(i * G * per, (i + 1) * G * per)
+        Kc, Vc = K[:, :, c:c + 1], V[:, :, c:c + 1]
+        dY = dYg[:, :, hq]
+        if gated:
+            g = g_cols[:, :, cols]                       # [B, S, G*per]
+            dY = dY * g.reshape(B, S, G, per)            # through the product, to Y
+        dq, dk, dv = sdpa_backward(Q[:, :, hq], Kc, Vc, dY)
+        out["dQ"][:, :, loc] = dq
+        out["dK"][:, :, i] = dk[:, :, 0]
+        out["dV"][:, :, i] = dv[:, :, 0]
+        if gated:
+            Y = sdpa(Q[:, :, hq], Kc, Vc)                # [B, S, G, D]
+            dgv = dYg[:, :, hq] * Y                      # to the gate, per (head, dim)
+            dg = dgv.sum(axis=-1) if mode == "headwise" else dgv.reshape(B, S, G * D)
+            dZ = dg * g * (1.0 - g)                      # through σ
+            out["dW"][:, cols] = X.reshape(B * S, -1).T @ dZ.reshape(B * S, -1)
+    if gated:
+        Yr = sdpa(Q, K, V, rows=rows)[:, rows]           # [B, R, Hq, D]
+        gr = sigmoid(gate_scores(X[:, rows], W))         # [B, R, N]
+        dgv = dYg[:, rows] * Yr
+        dg = dgv.sum(axis=-1) if mode == "headwise" else dgv.reshape(B, len(rows), Hq * D)
+        dZ = dg * gr * (1.0 - gr)
+        out["dX"] = dZ @ W.T
+    return out

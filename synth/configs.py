@@ -65,6 +65,16 @@ class Config:
     def total_flops(self) -> int:
         return self.attention_flops() + self.gate_flops()
 
+    # Backward, counted the same way: the four products the gradients need
+    # (dP = dY·Vᵀ, dV = Pᵀ·dY, dQ = dS·K, dK = dSᵀ·Q: 8*D flops per causal pair;
+    # recomputing S = Q·Kᵀ is not counted) plus the gate branch's two products
+    # (dX = dZ·W_θᵀ and dW_θ = Xᵀ·dZ, 2*M*d_model*N flops each).
+    def backward_attention_flops(self) -> int:
+        return 8 * self.D * self.B * self.Hq * self.causal_pairs()
+
+    def backward_flops(self) -> int:
+        return self.backward_attention_flops() + 2 * self.gate_flops()
+
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "fp32" else 2
 

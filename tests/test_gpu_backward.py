@@ -164,3 +164,34 @@ def test_backward_is_deterministic():
     for n in ("dQ", "dK", "dV", "dX"):
         assert torch.equal(_bits(a[n]), _bits(b[n])), n
     assert torch.equal(a["dW"].cpu(), b["dW"].cpu())
+
+
+# --------------------------------------------------------------- full workload size, sampled
+def test_backward_dense_prefill_full_size_sampled():
+    """gsa_backward on the whole dense-prefill workload (B 2, S 4096, 16/16 heads,
+    D 128, d_model 2048, elementwise gate), in the configuration the bench
+    times; the oracle computes two key/value heads' dQ, dK, dV, their dW_θ
+    columns (every token) and a sample of dX rows exactly."""
+    from helpers import sample_rows
+    cfg = CONFIGS["dense_prefill"]
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    dY = make_grad(cfg, seed=0, device=DEV)
+    out = run_backward(inp, dY, cfg.mode)
+    kv = [0, cfg.Hkv - 1]
+    rows = sample_rows(cfg.S)
+    ref = oracle.gated_sdpa_backward_sampled(f64(inp["X"]), f64(inp["W"]), f64(inp["Q"]), f64(inp["K"]),
+                                             f64(inp["V"]), f64(dY), cfg.mode, kv, rows)
+    qh = torch.as_tensor(ref["q_heads"])
+    pieces = {
+        "dQ": f64(out["dQ"][:, :, qh.to(DEV)]),
+        "dK": f64(out["dK"][:, :, kv]),
+        "dV": f64(out["dV"][:, :, kv]),
+        "dW": f64(out["dW"][:, torch.as_tensor(ref["w_cols"]).to(DEV)]),
+        "dX": f64(out["dX"][:, torch.as_tensor(rows).to(DEV)]),
+    }
+    for n, got in pieces.items():
+        want = ref[n]
+        report(got, want, bwd_tol(want), f"dense_prefill {n}")
+        rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+        print(f"  dense_prefill {n}: rel_fro={rel:.3e}", flush=True)
+        assert rel <= 1e-2

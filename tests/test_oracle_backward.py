@@ -129,3 +129,28 @@ def test_zero_gate_weight():
     assert np.max(np.abs(got["dW"] - t["X"][0].T @ dg / 4)) <= 1e-14
     dQ, dK, dV = oracle.sdpa_backward(t["Q"], t["K"], t["V"], t["dYg"] / 2)
     assert np.max(np.abs(got["dV"] - dV)) <= 1e-15
+
+
+@pytest.mark.parametrize("mode", ["elementwise", "headwise", "none"])
+def test_sampled_backward_equals_the_full_one(mode):
+    """The sampled form (used at full workload sizes) is the full backward's
+    result restricted to the chosen heads, gate columns and rows."""
+    rng = np.random.default_rng(31)
+    B, S, Hq, Hkv, D, dm = 2, 37, 6, 3, 8, 12
+    t = draw(rng, B, S, Hq, Hkv, D, dm, mode)
+    X, W, Q, K, V, dY = (t[k] for k in ("X", "W", "Q", "K", "V", "dYg"))
+    full = oracle.gated_sdpa_backward(X, W, Q, K, V, dY, mode)
+    kv, rows = [2, 0], [0, 5, 36]
+    part = oracle.gated_sdpa_backward_sampled(X, W, Q, K, V, dY, mode, kv, rows)
+    G = Hq // Hkv
+    assert list(part["q_heads"]) == [4, 5, 0, 1]
+    np.testing.assert_allclose(part["dQ"], full["dQ"][:, :, part["q_heads"]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dK"], full["dK"][:, :, kv], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dV"], full["dV"][:, :, kv], rtol=1e-12, atol=1e-12)
+    if mode == "none":
+        assert part["dW"] is None and part["dX"] is None
+        return
+    per = D if mode == "elementwise" else 1
+    assert len(part["w_cols"]) == G * len(kv) * per
+    np.testing.assert_allclose(part["dW"], full["dW"][:, part["w_cols"]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dX"], full["dX"][:, rows], rtol=1e-12, atol=1e-12)
