@@ -79,14 +79,15 @@ def test_mutant_is_caught(name):
 BWD_SRC = os.path.join(os.path.dirname(SRC), "backward.py")
 
 BWD_MUTANTS = {
-    "sigmoid_derivative_dropped": ("dZ = dg * g * (1.0 - g)", "dZ = dg * g"),
+    "sigmoid_derivative_dropped": ("    dZ = dg * g * (1.0 - g)                        #", "    dZ = dg * g  #"),
     "softmax_row_term_dropped": ("dS = P * (dP - (dP * P).sum(axis=-1, keepdims=True))", "dS = P * dP"),
     "dk_unscaled": ("dK[b, :, c, :] += (dS.T @ q) * scale", "dK[b, :, c, :] += dS.T @ q"),
     "dq_uses_values": ("dQ[b, :, h, :] = (dS @ Kc) * scale", "dQ[b, :, h, :] = (dS @ Vc) * scale"),
     "dv_untransposed_probs": ("dV[b, :, c, :] += P.T @ dy", "dV[b, :, c, :] += P @ dy"),
     "upstream_not_gated": ("dY = dYg * gv ", "dY = dYg "),
     "gate_grad_uses_gated_output": ("dgv = dYg * Y ", "dgv = dYg * Y * gv "),
-    "headwise_mean_not_sum": ("dg = dgv.sum(axis=-1)", "dg = dgv.mean(axis=-1)"),
+    "headwise_mean_not_sum": ("dg = dgv.sum(axis=-1)                      # one gate",
+                              "dg = dgv.mean(axis=-1)  # one gate"),
     "gqa_interleaved": ("c = h // G", "c = h % Hkv"),
     "dw_not_summed_over_batch": ("dW = X.reshape(B * S, -1).T @ dZ.reshape(B * S, -1)", "dW = X[0].T @ dZ[0]"),
     "bwd_mask_excludes_self": ("<= (np.arange(S) + off)[:, None]", "< (np.arange(S) + off)[:, None]"),
