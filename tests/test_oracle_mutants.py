@@ -146,3 +146,59 @@ def test_unmutated_backward_copy_passes():
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
 def test_backward_mutant_is_caught(name):
     assert not bwd_pins_pass(load_bwd_mutant(name))
+
+
+# --------------------------------------------------------------- first-token attention
+DIAG_SRC = os.path.join(os.path.dirname(SRC), "diagnostics.py")
+DIAG_MUTANTS = {
+    "fattn_unscaled": ("/ np.sqrt(D)", ""),
+    "fattn_interleaved_gqa": ("K[:, 0, h // G, :]", "K[:, 0, h % Hkv, :]"),
+    "fattn_last_key": ("K[:, 0, h // G, :]", "K[:, -1, h // G, :]"),
+    "fattn_log_not_exp": ("np.exp(s0 - lse[:, h, :])", "(s0 - lse[:, h, :])"),
+    "fattn_mean_over_heads_only": ("F.mean(axis=(0, 2))", "F.mean(axis=(0, 1))[:Hq]"),
+}
+
+
+def load_diag_mutant(name):
+    with open(DIAG_SRC) as f:
+        src = f.read().replace("from .gated_sdpa import", "from oracle.gated_sdpa import")
+    if name is not None:
+        old, new = DIAG_MUTANTS[name]
+        assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_diag_mutant_{name}")
+    exec(compile(src, f"<diag mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def diag_pins_pass(orc):
+    """Brute-force loops on a tiny GQA shape (per-row shares and per-head means)."""
+    rng = np.random.default_rng(23)
+    B, S, Hq, Hkv, D = 2, 7, 4, 2, 3
+    Q, K, V = (rng.standard_normal((B, S, Hq, D)), rng.standard_normal((B, S, Hkv, D)),
+               rng.standard_normal((B, S, Hkv, D)))
+    try:
+        F, head_mean, mean = orc.first_token_attention(Q, K, V)
+    except Exception:
+        return False
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                s = [math.fsum(Q[b, i, h, d] * K[b, j, h // G, d] for d in range(D)) / math.sqrt(D)
+                     for j in range(i + 1)]
+                want = math.exp(s[0]) / math.fsum(math.exp(x) for x in s)
+                if not abs(F[b, h, i] - want) <= 1e-12:
+                    return False
+    want_h = [math.fsum(F[b, h, i] for b in range(B) for i in range(S)) / (B * S) for h in range(Hq)]
+    return (np.shape(head_mean) == (Hq,) and np.allclose(head_mean, want_h, rtol=0, atol=1e-14)
+            and abs(mean - math.fsum(want_h) / Hq) <= 1e-14)
+
+
+def test_unmutated_diagnostics_copy_passes():
+    assert diag_pins_pass(load_diag_mutant(None))
+
+
+@pytest.mark.parametrize("name", sorted(DIAG_MUTANTS))
+def test_diagnostics_mutant_is_caught(name):
+    assert not diag_pins_pass(load_diag_mutant(name))
