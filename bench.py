@@ -9,8 +9,9 @@ Reported (one JSON line): whole-step TFLOP/s; the roofline of the dominant
 kernel (the gated forward), timed per launch with HIP events on the stream it
 runs on; the decode workload (batch 64, one token against a 16384-long KV
 cache, 32/8 heads) as GB/s with its own roofline; the backward of the prefill
-path (gsa_backward) as TFLOP/s; and the fp64 oracle timed on the host cores on
-a bounded sample of the prefill workload.
+path (gsa_backward) as TFLOP/s; the first-token attention diagnostic on the
+32k sink-mimicking workload as GB/s; and the fp64 oracle timed on the host
+cores on a bounded sample of the prefill workload.
 """
 import argparse
 import hashlib
@@ -36,10 +37,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-decode", action="store_true", help="skip the decode workload")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "backward", "diagnostic"], default=None,
                    help="run one workload's GPU part only (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     p.add_argument("--no-backward", action="store_true", help="skip the backward workload")
+    p.add_argument("--no-diagnostic", action="store_true",
+                   help="skip the first-token attention diagnostic on the long_prefill workload")
     p.add_argument("--no-others", action="store_true",
                    help="skip the gqa_prefill and long_prefill lines (reported beside the headline)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -189,7 +192,8 @@ def backward_bench(args, torch, gsa, cfg):
     def step():
         holder["g"] = gsa.backward(X, W, G, Q, K, V, Y, LSE, dY, cfg.mode, workspace=ws)
 
-    ms, _, wall = time_steps(step, step, args.steps, args.warmup, torch)
+    # the timed unit is the whole call, so there is no separate kernel-only pass
+    ms, _, wall = time_steps(step, lambda: None, args.steps, args.warmup, torch)
     for n in ("dQ", "dK", "dV", "dX", "dW"):
         if not torch.isfinite(holder["g"][n][:64].float()).all():
             raise RuntimeError(f"non-finite {n}")
@@ -206,6 +210,42 @@ def backward_bench(args, torch, gsa, cfg):
             "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "avg_launch_ms": ms,
             "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+
+def diagnostic_bench(args, torch, gsa, cfg):
+    """gsa_first_token_attention (F = exp(q_i·k_0/√D − LSE_i) per head and row, plus
+    per-head means) on the long_prefill workload, whose token-0 keys are scaled ×8
+    to mimic an attention sink.  HBM-bound: Q is read once, LSE read and F
+    written once."""
+    from synth import make_inputs
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    G = gsa.gate_logits(X, W)
+    _, LSE = gsa.forward_lse(Q, K, V, G, cfg.mode)
+    del G, X
+    holder = {}
+
+    def step():
+        holder["r"] = gsa.first_token_attention(Q, K, LSE)
+
+    ms, _, wall = time_steps(step, lambda: None, args.steps, args.warmup, torch)
+    F, means = holder["r"]
+    e = cfg.elem_bytes()
+    rows = cfg.B * cfg.Hq * cfg.S
+    nbytes = rows * cfg.D * e + rows * 4 * 2 + cfg.B * cfg.Hkv * cfg.D * e
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": cfg.name, "metric": "first-token attention share, GB/s (% of HBM peak)",
+        "value": achieved, "unit": "GB/s", "ms_per_step": ms,
+        "mean_first_token_share": float(means[-1].item()),
+        "config": {"B": cfg.B, "S": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "token0_key_scale": cfg.sink_scale},
+        "roofline": {
+            "kernel": "first_token_share_kernel (+ head means)", "bound": "hbm", "achieved": achieved,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes,
         },
     }
 
@@ -277,7 +317,17 @@ def main():
     pcfg = CONFIGS["dense_prefill"]
     dcfg = CONFIGS["decode"]
     out = None
-    if args.only != "decode":
+    if args.only == "diagnostic":
+        dg = diagnostic_bench(args, torch, gsa, CONFIGS["long_prefill"])
+        print(json.dumps(dict(dg, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
+                              scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")), flush=True)
+        return
+    if args.only == "backward":
+        bwd = backward_bench(args, torch, gsa, pcfg)
+        print(json.dumps(dict(bwd, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
+                              scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")), flush=True)
+        return
+    if args.only not in ("decode",):
         pre = prefill_bench(args, torch, gsa, pcfg)
         print(f"# prefill: {pre['ms_per_step']:.4f} ms/step, {pre['tflops']:.1f} TFLOP/s; forward "
               f"{pre['roofline']['avg_launch_ms']:.4f} ms = {pre['roofline']['achieved']:.1f} TFLOP/s",
@@ -313,6 +363,12 @@ def main():
         print(f"# backward: {bwd['ms_per_step']:.4f} ms/step, {bwd['value']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
         out["backward"] = bwd
+    if out is not None and not args.no_diagnostic and args.only is None:
+        dg = diagnostic_bench(args, torch, gsa, CONFIGS["long_prefill"])
+        torch.cuda.empty_cache()
+        print(f"# first-token share (long_prefill): {dg['ms_per_step']*1e3:.1f} us, {dg['value']:.0f} GB/s, "
+              f"mean share {dg['mean_first_token_share']:.4f}", file=sys.stderr, flush=True)
+        out["first_token_attention"] = dg
     if out is not None and not args.no_others and args.only is None:
         # the other prefill workloads, each its own gate GEMM + forward step
         others = {}

@@ -28,6 +28,8 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
                            int mode, hipStream_t stream);
 int bwd_kv_slices(int B, int S, int Hq, int Hkv);
+hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
+                                    int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 int bwd_stat_rows(int S);
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
                               int64_t N, hipStream_t st);
@@ -346,6 +348,22 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
     if (e != hipSuccess) return hip_result(e, "gsa_backward dW launch");
   }
   return ok();
+}
+
+gsa_status gsa_first_token_attention(const void* Q, const void* K, const float* LSE, float* F,
+                                     float* head_mean, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int dtype, void* stream) {
+  const char* fn = "gsa_first_token_attention";
+  if (!Q || !K || !LSE || !F) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (gsa_status st = check_attn_shape(fn, B, S, Hq, Hkv, D, GSA_GATE_NONE, nullptr)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (!aligned16(Q) || !aligned16(K)) return fail(GSA_ERR_MISALIGNED, "%s: Q and K must be 16-byte aligned", fn);
+  if (((uintptr_t)LSE | (uintptr_t)F | (uintptr_t)head_mean) % 4 != 0)
+    return fail(GSA_ERR_MISALIGNED, "%s: LSE, F and head_mean must be 4-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_first_token_share(Q, K, LSE, F, head_mean, (int)B, (int)S, (int)Hq, (int)Hkv,
+                                                  (int)D, dtype == GSA_BF16, (hipStream_t)stream),
+                    fn);
 }
 
 }  // extern "C"

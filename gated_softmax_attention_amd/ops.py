@@ -167,6 +167,25 @@ def backward(X, W, G, Q, K, V, Y, LSE, dY, mode, workspace=None, stream=None):
     return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dX, "dW": dW}
 
 
+def first_token_attention(Q, K, LSE, with_means=True, stream=None):
+    """Share of attention each query row gives token 0, F [B, Hq, S] float32, from
+    the LSE of forward_lse on the same Q and K.  With with_means also returns the
+    per-head means over batches and rows followed by their mean (Hq + 1 floats)."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D):
+        raise ValueError("K must be [B, S, Hkv, D] matching Q")
+    if LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S:
+        raise ValueError("LSE must be float32 with B*Hq*S elements")
+    F = torch.empty((B, Hq, S), dtype=torch.float32, device=Q.device)
+    means = torch.empty(Hq + 1, dtype=torch.float32, device=Q.device) if with_means else None
+    lib = _lib.load()
+    _lib.check(lib.gsa_first_token_attention(_dev(Q, "Q"), _dev(K, "K"), _dev(LSE, "LSE"), _dev(F, "F"),
+                                             None if means is None else _dev(means, "head_mean"),
+                                             B, S, Hq, Hkv, D, _dtype(Q, K), _stream(stream)))
+    return (F, means) if with_means else F
+
+
 def gated_attention(X, W, Q, K, V, mode, stream=None):
     """The whole prefill path: gate projection + sigmoid, then causal gated SDPA."""
     G = None if mode == "none" else gate_logits(X, W, stream=stream)

@@ -176,6 +176,23 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
                         int64_t Hkv, int64_t D, int64_t d_model, int mode, int dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * First-token attention share ("GatedAttention [2025]" §1.4.3, the F-Attn
+ * column of Table 4; "10 · 门控" §3.4): the causal softmax probability each
+ * query row gives token 0,
+ *   F[b,h,i] = exp(Q[b,i,h,:]·K[b,0,c,:] / √D − LSE[b,h,i]),  c = h / (Hq/Hkv),
+ * from the LSE a gsa_forward_lse call on the same Q and K wrote.
+ *   Q : [B, S, Hq, D], K : [B, S, Hkv, D] (dtype; only key row 0 is read)
+ *   LSE : [B, Hq, S] float32 (input)    F : [B, Hq, S] float32 (output)
+ *   head_mean : NULL, or Hq + 1 floats (output): the mean of F over batches and
+ *     rows for each head, then the mean of those Hq values.
+ * Same shape rules as gsa_forward; LSE, F and head_mean 4-byte aligned.
+ * Deterministic (fixed-order sums).
+ */
+gsa_status gsa_first_token_attention(const void* Q, const void* K, const float* LSE, float* F,
+                                     float* head_mean, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int dtype, void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

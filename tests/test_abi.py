@@ -179,6 +179,22 @@ def test_backward_workspace_arithmetic(lib):
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 64, 9) == 0
 
 
+def test_first_token_attention_argument_checks(lib):
+    def fa(Q=FAKE, K=FAKE, LSE=FAKE, F=FAKE, hm=None, B=1, S=8, Hq=4, Hkv=2, D=128, dtype=1):
+        return lib.gsa_first_token_attention(Q, K, LSE, F, hm, B, S, Hq, Hkv, D, dtype, None)
+    assert fa(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert fa(LSE=None) == _lib.GSA_ERR_INVALID_ARG
+    assert fa(F=None) == _lib.GSA_ERR_INVALID_ARG
+    assert fa(S=0) == _lib.GSA_ERR_INVALID_ARG
+    assert fa(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert fa(D=32) == _lib.GSA_ERR_UNSUPPORTED
+    assert fa(dtype=4) == _lib.GSA_ERR_UNSUPPORTED
+    assert fa(K=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert fa(F=FAKE + 2) == _lib.GSA_ERR_MISALIGNED
+    assert fa(hm=FAKE + 1) == _lib.GSA_ERR_MISALIGNED
+    assert lib.gsa_last_error_message().decode().startswith("gsa_first_token_attention")
+
+
 @pytest.mark.skipif("have_gpu()", reason="a GPU is visible: valid-looking fake pointers must not be launched")
 def test_valid_arguments_without_a_gpu_report_no_device(lib):
     assert fwd(lib) == _lib.GSA_ERR_NO_DEVICE

@@ -84,3 +84,13 @@ def test_sink_key_takes_the_mass():
     K[:, 0] = 50.0
     F, _, _ = oracle.first_token_attention(Q, K, V)
     assert np.all(F[:, :, 1:] > 1 - 1e-9)
+
+
+def test_row_subset_equals_full():
+    Q, K, V = draw(np.random.default_rng(7), 2, 50, 4, 2, 8)
+    F, _, _ = oracle.first_token_attention(Q, K, V)
+    rows = [0, 3, 17, 49]
+    Fr, hm, m = oracle.first_token_attention(Q, K, V, rows=rows)
+    assert hm is None and m is None
+    assert np.array_equal(Fr[:, :, rows], F[:, :, rows])
+    assert np.isnan(np.delete(Fr, rows, axis=2)).all()

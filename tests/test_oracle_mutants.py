@@ -154,7 +154,7 @@ DIAG_MUTANTS = {
     "fattn_unscaled": ("/ np.sqrt(D)", ""),
     "fattn_interleaved_gqa": ("K[:, 0, h // G, :]", "K[:, 0, h % Hkv, :]"),
     "fattn_last_key": ("K[:, 0, h // G, :]", "K[:, -1, h // G, :]"),
-    "fattn_log_not_exp": ("np.exp(s0 - lse[:, h, :])", "(s0 - lse[:, h, :])"),
+    "fattn_log_not_exp": ("np.exp(s0 - lse[:, h, r])", "(s0 - lse[:, h, r])"),
     "fattn_mean_over_heads_only": ("F.mean(axis=(0, 2))", "F.mean(axis=(0, 1))[:Hq]"),
 }
 
