@@ -61,6 +61,24 @@ def make_grad(cfg: Config, seed: int = 0, device="cpu"):
     return _randn((cfg.B, cfg.S, cfg.Hq, cfg.D), gen, device, _DT[cfg.dtype])
 
 
+def make_projection(cfg: Config, W, seed: int = 0, device="cpu"):
+    """Projection weights W_Q [dm, Hq·D], W_K and W_V [dm, Hkv·D] ~ N(0, 1/dm) (variance,
+    as W_θ) in the config's dtype, from their own generator seeded with
+    ``seed + 2_000_003`` (drawn in that order), and the concatenation
+    [W_Q | W_K | W_V | W] the fused projection reads (W is the gate weight from
+    make_inputs; None for no gate)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 2_000_003)
+    dt = _DT[cfg.dtype]
+    sc = 1.0 / math.sqrt(cfg.d_model)
+    Wq = _randn((cfg.d_model, cfg.Hq * cfg.D), gen, device, dt, scale=sc)
+    Wk = _randn((cfg.d_model, cfg.Hkv * cfg.D), gen, device, dt, scale=sc)
+    Wv = _randn((cfg.d_model, cfg.Hkv * cfg.D), gen, device, dt, scale=sc)
+    parts = [Wq, Wk, Wv] + ([] if W is None else [W])
+    return {"Wq": Wq, "Wk": Wk, "Wv": Wv, "Wcat": torch.cat(parts, dim=1).contiguous()}
+
+
 def make_decode_inputs(cfg: Config, seed: int = 0, device="cpu"):
     """Decode inputs: X [B,1,dm], W, Q [B,1,Hq,D], K,V cache [B,L,Hkv,D]."""
     assert cfg.decode

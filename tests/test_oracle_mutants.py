@@ -202,3 +202,66 @@ def test_unmutated_diagnostics_copy_passes():
 @pytest.mark.parametrize("name", sorted(DIAG_MUTANTS))
 def test_diagnostics_mutant_is_caught(name):
     assert not diag_pins_pass(load_diag_mutant(name))
+
+
+# --------------------------------------------------------------- fused input projection
+PROJ_SRC = os.path.join(os.path.dirname(SRC), "projection.py")
+PROJ_MUTANTS = {
+    "proj_heads_transposed": ("np.asarray(Wq, dtype=np.float64)).reshape(B, S, Hq, D)",
+                              "np.asarray(Wq, dtype=np.float64)).reshape(B, S, D, Hq).transpose(0, 1, 3, 2)"),
+    "proj_keys_from_values": ("K = (X @ np.asarray(Wk,", "K = (X @ np.asarray(Wv,"),
+    "proj_gate_without_sigmoid": ("G = None if W is None else sigmoid(gate_scores(X, W))",
+                                  "G = None if W is None else gate_scores(X, W)"),
+    "proj_weights_transposed": ("V = (X @ np.asarray(Wv, dtype=np.float64))",
+                                "V = (X @ np.asarray(Wv, dtype=np.float64).T.T[:, ::-1])"),
+}
+
+
+def load_proj_mutant(name):
+    with open(PROJ_SRC) as f:
+        src = f.read().replace("from .gated_sdpa import", "from oracle.gated_sdpa import")
+    if name is not None:
+        old, new = PROJ_MUTANTS[name]
+        assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_proj_mutant_{name}")
+    exec(compile(src, f"<proj mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def proj_pins_pass(orc):
+    """Brute-force loops on a tiny GQA shape."""
+    rng = np.random.default_rng(29)
+    B, S, dm, Hq, Hkv, D, N = 2, 3, 5, 4, 2, 3, 6
+    X = rng.standard_normal((B, S, dm))
+    Wq, Wk, Wv, W = (rng.standard_normal((dm, w)) for w in (Hq * D, Hkv * D, Hkv * D, N))
+    try:
+        Q, K, V, G = orc.project_qkvg(X, Wq, Wk, Wv, W, Hq, Hkv, D)
+    except Exception:
+        return False
+    for b in range(B):
+        for i in range(S):
+            for h in range(Hq):
+                for d in range(D):
+                    if abs(Q[b, i, h, d] - math.fsum(X[b, i, k] * Wq[k, h * D + d] for k in range(dm))) > 1e-12:
+                        return False
+            for c in range(Hkv):
+                for d in range(D):
+                    if abs(K[b, i, c, d] - math.fsum(X[b, i, k] * Wk[k, c * D + d] for k in range(dm))) > 1e-12:
+                        return False
+                    if abs(V[b, i, c, d] - math.fsum(X[b, i, k] * Wv[k, c * D + d] for k in range(dm))) > 1e-12:
+                        return False
+            for n in range(N):
+                z = math.fsum(X[b, i, k] * W[k, n] for k in range(dm))
+                if abs(G[b, i, n] - 1 / (1 + math.exp(-z))) > 1e-14:
+                    return False
+    return True
+
+
+def test_unmutated_projection_copy_passes():
+    assert proj_pins_pass(load_proj_mutant(None))
+
+
+@pytest.mark.parametrize("name", sorted(PROJ_MUTANTS))
+def test_projection_mutant_is_caught(name):
+    assert not proj_pins_pass(load_proj_mutant(name))
