@@ -9,7 +9,8 @@ Reported (one JSON line): whole-step TFLOP/s; the roofline of the dominant
 kernel (the gated forward), timed per launch with HIP events on the stream it
 runs on; the decode workload (batch 64, one token against a 16384-long KV
 cache, 32/8 heads) as GB/s with its own roofline; the backward of the prefill
-path (gsa_backward) as TFLOP/s; the first-token attention diagnostic on the
+path (gsa_backward) as TFLOP/s; the fused Q/K/V/gate projection as TFLOP/s;
+the first-token attention diagnostic on the
 32k sink-mimicking workload as GB/s; and the fp64 oracle timed on the host
 cores on a bounded sample of the prefill workload.
 """
@@ -37,10 +38,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-decode", action="store_true", help="skip the decode workload")
-    p.add_argument("--only", choices=["prefill", "decode", "backward", "diagnostic"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "backward", "diagnostic", "projection"], default=None,
                    help="run one workload's GPU part only (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     p.add_argument("--no-backward", action="store_true", help="skip the backward workload")
+    p.add_argument("--no-projection", action="store_true", help="skip the fused input projection")
     p.add_argument("--no-diagnostic", action="store_true",
                    help="skip the first-token attention diagnostic on the long_prefill workload")
     p.add_argument("--no-others", action="store_true",
@@ -214,6 +216,37 @@ def backward_bench(args, torch, gsa, cfg):
     }
 
 
+def projection_bench(args, torch, gsa, cfg):
+    """gsa_project_qkvg: Q, K, V and σ(X·W_θ) from one GEMM over X on the prefill
+    workload (W = [W_Q | W_K | W_V | W_θ]).  MFMA-bound: 2·M·d_model·N flop."""
+    from synth import make_inputs, make_projection
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    pw = make_projection(cfg, inp["W"], seed=0, device="cuda:0")
+    X, Wcat = inp["X"], pw["Wcat"]
+    ng = inp["W"].shape[1]
+    del inp, pw
+    holder = {}
+
+    def step():
+        holder["r"] = gsa.project_qkvg(X, Wcat, cfg.Hq, cfg.Hkv, cfg.D, ng)
+
+    ms, _, wall = time_steps(step, lambda: None, args.steps, args.warmup, torch)
+    M, N = cfg.B * cfg.S, Wcat.shape[1]
+    flops = 2 * M * cfg.d_model * N
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": cfg.name, "metric": "fused Q/K/V/gate projection TFLOP/s (% of bf16 MFMA peak)",
+        "value": achieved, "unit": "TFLOP/s", "ms_per_step": ms, "pct_of_peak": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "config": {"M": M, "d_model": cfg.d_model, "N": N, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "gate_width": ng, "flops_per_step": flops},
+        "roofline": {
+            "kernel": "gate_gemm_bf16_big_kernel<true> (routing epilogue)", "bound": "mfma", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+
 def diagnostic_bench(args, torch, gsa, cfg):
     """gsa_first_token_attention (F = exp(q_i·k_0/√D − LSE_i) per head and row, plus
     per-head means) on the long_prefill workload, whose token-0 keys are scaled ×8
@@ -317,6 +350,11 @@ def main():
     pcfg = CONFIGS["dense_prefill"]
     dcfg = CONFIGS["decode"]
     out = None
+    if args.only == "projection":
+        pj = projection_bench(args, torch, gsa, pcfg)
+        print(json.dumps(dict(pj, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
+                              scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")), flush=True)
+        return
     if args.only == "diagnostic":
         dg = diagnostic_bench(args, torch, gsa, CONFIGS["long_prefill"])
         print(json.dumps(dict(dg, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
@@ -363,6 +401,12 @@ def main():
         print(f"# backward: {bwd['ms_per_step']:.4f} ms/step, {bwd['value']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
         out["backward"] = bwd
+    if out is not None and not args.no_projection and args.only is None:
+        pj = projection_bench(args, torch, gsa, pcfg)
+        torch.cuda.empty_cache()
+        print(f"# projection: {pj['ms_per_step']*1e3:.1f} us, {pj['value']:.0f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        out["projection"] = pj
     if out is not None and not args.no_diagnostic and args.only is None:
         dg = diagnostic_bench(args, torch, gsa, CONFIGS["long_prefill"])
         torch.cuda.empty_cache()

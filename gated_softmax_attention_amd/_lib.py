@@ -34,6 +34,7 @@ SIGNATURES = {
     "gsa_decode": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
     "gsa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64, _I]),
     "gsa_backward": (_I, [_P] * 14 + [_I64] * 6 + [_I, _I, _P, _SZ, _P]),
+    "gsa_project_qkvg": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P]),
     "gsa_first_token_attention": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
 }
 

@@ -28,6 +28,8 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
                            int mode, hipStream_t stream);
 int bwd_kv_slices(int B, int S, int Hq, int Hkv);
+hipError_t launch_project_qkvg(const void* X, const void* W, void* Q, void* Kp, void* V, float* G, int64_t M,
+                               int64_t K, int64_t nq, int64_t nkv, int64_t ng, hipStream_t stream);
 hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 int bwd_stat_rows(int S);
@@ -348,6 +350,32 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
     if (e != hipSuccess) return hip_result(e, "gsa_backward dW launch");
   }
   return ok();
+}
+
+gsa_status gsa_project_qkvg(const void* X, const void* W, void* Q, void* K, void* V, float* G, int64_t M,
+                            int64_t d_model, int64_t Hq, int64_t Hkv, int64_t D, int64_t n_gate, int dtype,
+                            void* stream) {
+  const char* fn = "gsa_project_qkvg";
+  if (!X || !W || !Q || !K || !V) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (M <= 0 || d_model <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || n_gate < 0)
+    return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive (n_gate >= 0)", fn);
+  if (Hq % Hkv != 0)
+    return fail(GSA_ERR_INVALID_ARG, "%s: Hq=%lld is not a multiple of Hkv=%lld", fn, (long long)Hq,
+                (long long)Hkv);
+  if ((n_gate == 0) != (G == nullptr))
+    return fail(GSA_ERR_INVALID_ARG, "%s: G must be NULL exactly when n_gate is 0", fn);
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "%s: only GSA_BF16 is supported", fn);
+  const int64_t nq = Hq * D, nkv = Hkv * D, N = nq + 2 * nkv + n_gate;
+  if (d_model % 8 != 0 || nq % 8 != 0 || nkv % 8 != 0 || n_gate % 8 != 0)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: d_model and every output width must be multiples of 8", fn);
+  if (M * d_model * 2 >= kIntMax || d_model * N * 2 >= kIntMax || M > kIntMax)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: X or W exceeds 2 GiB", fn);
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Q) || !aligned16(K) || !aligned16(V) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "%s: X, W, Q, K, V and G must be 16-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_project_qkvg(X, W, Q, K, V, G, M, d_model, nq, nkv, n_gate, (hipStream_t)stream),
+                    fn);
 }
 
 gsa_status gsa_first_token_attention(const void* Q, const void* K, const float* LSE, float* F,

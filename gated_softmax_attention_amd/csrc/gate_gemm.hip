@@ -160,10 +160,21 @@ constexpr int WSL = BN / 8;       // 32 slots per W row
 constexpr uint32_t kOOB = 0xfffffff0u;  // an offset past any buffer: reads zeros
 }  // namespace gemm_big
 
+// Where the fused input projection's output columns go: [0, nq) to Q,
+// [nq, nq + nkv) to K, [nq + nkv, nq + 2·nkv) to V (bf16, row-major with those
+// widths) and the rest to G (σ, float32).
+struct ProjOut {
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  int nq, nkv;
+};
+
+template <bool ROUTE>
 __global__ __launch_bounds__(512, 1)
 void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                                float* __restrict__ G, int M, int K, int N, int tiles_m, int tiles_n,
-                               int apply_sigmoid) {
+                               int apply_sigmoid, ProjOut po) {
   using namespace gemm_big;
   __shared__ __align__(16) bf16 Xs[2][BM * XSL * 8];
   __shared__ __align__(16) bf16 Ws[2][BK * WSL * 8];
@@ -317,20 +328,57 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
 
   // epilogue: lane holds column l32 of each 32x32 block, rows 8*(r/4) + 4*hl + r%4
   const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+  if constexpr (!ROUTE) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = n0 + wn * 64 + nt * 32 + l32;
+        const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + 8 * (r >> 2) + (r & 3);
+          const float z = acc[mt][nt][r];
+          const float v = apply_sigmoid ? sigmoidf(z) : z;
+          if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
+        }
+      }
+  } else {
+    const int ng = N - po.nq - 2 * po.nkv;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = n0 + wn * 64 + nt * 32 + l32;
-      const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
+      // this lane's column: destination, its row width and the column within it
+      bf16* dst = po.q;
+      int ld = po.nq, col = n;
+      if (n >= po.nq + 2 * po.nkv) {
+        dst = nullptr;
+        ld = ng;
+        col = n - po.nq - 2 * po.nkv;
+      } else if (n >= po.nq + po.nkv) {
+        dst = po.v;
+        ld = po.nkv;
+        col = n - po.nq - po.nkv;
+      } else if (n >= po.nq) {
+        dst = po.k;
+        ld = po.nkv;
+        col = n - po.nq;
+      }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mb + 8 * (r >> 2) + (r & 3);
-        const float z = acc[mt][nt][r];
-        const float v = apply_sigmoid ? sigmoidf(z) : z;
-        if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
+      for (int mt = 0; mt < 4; ++mt) {
+        const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + 8 * (r >> 2) + (r & 3);
+          const float z = acc[mt][nt][r];
+          if (full || (m < M && n < N)) {
+            if (dst != nullptr) dst[(int64_t)m * ld + col] = (bf16)z;
+            else G[(int64_t)m * ld + col] = sigmoidf(z);
+          }
+        }
       }
     }
+  }
 }
 
 // Narrow / short bf16 gate projection for shapes with few rows (decode: one
@@ -513,9 +561,9 @@ hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, i
       K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, gemm_big::BN);
     const int tiles_m = (int)ceil_div<int64_t>(M, gemm_big::BM);
-    hipLaunchKernelGGL(gate_gemm_bf16_big_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
+    hipLaunchKernelGGL(gate_gemm_bf16_big_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_m, tiles_n,
-                       (int)apply_sigmoid);
+                       (int)apply_sigmoid, ProjOut{nullptr, nullptr, nullptr, 0, 0});
   } else if (bf16_inputs && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) && K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, 32);
     const int64_t tiles = ceil_div<int64_t>(M, 32) * tiles_n;
@@ -535,6 +583,21 @@ hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, i
                        (const float*)X, (const float*)W, G, (int)M, (int)K, (int)N, tiles_n,
                        (int)apply_sigmoid);
   }
+  return hipGetLastError();
+}
+
+// Fused input projection: [Q | K | V | Z] = X · [W_Q | W_K | W_V | W_θ] in one
+// pass over X ("GatedAttention [2025]" §1.2.1 QKV projections and §1.2.2 gate
+// scores), Q/K/V rounded to bf16, G = σ(Z) in float32.  W is [K, N] with
+// N = nq + 2·nkv + ng; the large-tile kernel with the routing epilogue.
+hipError_t launch_project_qkvg(const void* X, const void* W, void* Q, void* Kp, void* V, float* G, int64_t M,
+                               int64_t K, int64_t nq, int64_t nkv, int64_t ng, hipStream_t stream) {
+  const int64_t N = nq + 2 * nkv + ng;
+  const int tiles_n = (int)ceil_div<int64_t>(N, gemm_big::BN);
+  const int tiles_m = (int)ceil_div<int64_t>(M, gemm_big::BM);
+  hipLaunchKernelGGL(gate_gemm_bf16_big_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
+                     (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_m, tiles_n, 1,
+                     ProjOut{(bf16*)Q, (bf16*)Kp, (bf16*)V, (int)nq, (int)nkv});
   return hipGetLastError();
 }
 

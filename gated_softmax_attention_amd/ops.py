@@ -167,6 +167,25 @@ def backward(X, W, G, Q, K, V, Y, LSE, dY, mode, workspace=None, stream=None):
     return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dX, "dW": dW}
 
 
+def project_qkvg(X, Wcat, Hq, Hkv, D, n_gate, stream=None):
+    """Q [.., Hq, D], K and V [.., Hkv, D] (bf16) and G = σ(Z) [M, n_gate] float32
+    (None when n_gate is 0) from X [..., d_model] and Wcat = [W_Q | W_K | W_V | W_θ]."""
+    dm = X.shape[-1]
+    M = X.numel() // dm
+    lead = tuple(X.shape[:-1])
+    if Wcat.shape != (dm, (Hq + 2 * Hkv) * D + n_gate):
+        raise ValueError("Wcat must be [d_model, Hq*D + 2*Hkv*D + n_gate]")
+    Q = torch.empty(lead + (Hq, D), dtype=X.dtype, device=X.device)
+    K = torch.empty(lead + (Hkv, D), dtype=X.dtype, device=X.device)
+    V = torch.empty(lead + (Hkv, D), dtype=X.dtype, device=X.device)
+    G = torch.empty((M, n_gate), dtype=torch.float32, device=X.device) if n_gate > 0 else None
+    lib = _lib.load()
+    _lib.check(lib.gsa_project_qkvg(_dev(X, "X"), _dev(Wcat, "Wcat"), _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"),
+                                    None if G is None else _dev(G, "G"), M, dm, Hq, Hkv, D, n_gate,
+                                    _dtype(X, Wcat), _stream(stream)))
+    return Q, K, V, G
+
+
 def first_token_attention(Q, K, LSE, with_means=True, stream=None):
     """Share of attention each query row gives token 0, F [B, Hq, S] float32, from
     the LSE of forward_lse on the same Q and K.  With with_means also returns the

@@ -177,6 +177,24 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Fused input projection: Q, K, V and the gate from one pass over X,
+ *   [Q | K | V | Z] = X · [W_Q | W_K | W_V | W_θ],   G = σ(Z)
+ * (the QKV projections of "GatedAttention [2025]" §1.2.1 and the gate scores of
+ * §1.2.2, which read the same X).  Head h of Q is columns h·D .. h·D+D−1 (so Q
+ * is [M, Hq·D] = [B, S, Hq, D]); likewise K and V with the Hkv key/value heads.
+ *   X : [M, d_model] bf16
+ *   W : [d_model, Hq·D + 2·Hkv·D + n_gate] bf16, the four weights side by side
+ *   Q : [M, Hq·D], K and V : [M, Hkv·D] bf16 outputs (rounded once)
+ *   G : [M, n_gate] float32 output σ(Z) (n_gate = Hq·D elementwise, Hq
+ *       headwise); NULL exactly when n_gate is 0 (no gate).
+ * Requires dtype GSA_BF16, d_model and every output width multiples of 8, and
+ * X and W below 2 GiB.
+ */
+gsa_status gsa_project_qkvg(const void* X, const void* W, void* Q, void* K, void* V, float* G, int64_t M,
+                            int64_t d_model, int64_t Hq, int64_t Hkv, int64_t D, int64_t n_gate, int dtype,
+                            void* stream);
+
+/*
  * First-token attention share ("GatedAttention [2025]" §1.4.3, the F-Attn
  * column of Table 4; "10 · 门控" §3.4): the causal softmax probability each
  * query row gives token 0,

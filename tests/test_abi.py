@@ -179,6 +179,23 @@ def test_backward_workspace_arithmetic(lib):
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 64, 9) == 0
 
 
+def test_project_qkvg_argument_checks(lib):
+    def pj(X=FAKE, W=FAKE, Q=FAKE, G=FAKE, M=16, dm=64, Hq=4, Hkv=2, D=128, ng=512, dtype=1):
+        return lib.gsa_project_qkvg(X, W, Q, FAKE, FAKE, G, M, dm, Hq, Hkv, D, ng, dtype, None)
+    assert pj(X=None) == _lib.GSA_ERR_INVALID_ARG
+    assert pj(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert pj(M=0) == _lib.GSA_ERR_INVALID_ARG
+    assert pj(ng=-8) == _lib.GSA_ERR_INVALID_ARG
+    assert pj(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert pj(G=None) == _lib.GSA_ERR_INVALID_ARG            # gate columns but no G
+    assert pj(ng=0) == _lib.GSA_ERR_INVALID_ARG              # G given without gate columns
+    assert pj(dtype=0) == _lib.GSA_ERR_UNSUPPORTED
+    assert pj(dm=60) == _lib.GSA_ERR_UNSUPPORTED
+    assert pj(ng=4) == _lib.GSA_ERR_UNSUPPORTED
+    assert pj(W=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert lib.gsa_last_error_message().decode().startswith("gsa_project_qkvg")
+
+
 def test_first_token_attention_argument_checks(lib):
     def fa(Q=FAKE, K=FAKE, LSE=FAKE, F=FAKE, hm=None, B=1, S=8, Hq=4, Hkv=2, D=128, dtype=1):
         return lib.gsa_first_token_attention(Q, K, LSE, F, hm, B, S, Hq, Hkv, D, dtype, None)
