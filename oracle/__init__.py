@@ -18,13 +18,16 @@ Sources (page titles; sections):
     view of the gate as [B, T, n_h, d_h] or [B, T, n_h, 1]).
 
 Every function here is pinned by tests in ``tests/test_oracle.py``,
-``tests/test_oracle_backward.py``, ``tests/test_oracle_diagnostics.py`` and
-``tests/test_oracle_projection.py`` (brute-force loops, central differences of the
+``tests/test_oracle_backward.py``, ``tests/test_oracle_diagnostics.py``,
+``tests/test_oracle_projection.py`` and ``tests/test_oracle_variants.py`` (brute-force loops, central differences of the
 brute-force forward, a library SDPA and a library autodiff in float64, closed
 forms and invariants); none is "parity unpinned".
 
 The backward (``backward.py``) is the chain rule on the plain forward; its gate
 branch follows the "Gated Attention如何用1%的参数量…" page, §2.2 gradient analysis.
+``variants.py`` holds the gating variants of the design space (§1.2.2 items
+(3)-(5), NS-sigmoid of §1.4.2, the per-head RMSNorm of §1.4.1, G2 value
+gating), pinned in ``tests/test_oracle_variants.py``.
 ``projection.py`` holds the fused input projection (§1.2.1 QKV projections plus the
 gate scores), pinned in ``tests/test_oracle_projection.py``.
 ``diagnostics.py`` holds the first-token attention share ("GatedAttention [2025]"
@@ -37,8 +40,9 @@ from .gated_sdpa import (
 from .backward import sdpa_backward, gated_sdpa_backward, gated_sdpa_backward_sampled
 from .diagnostics import first_token_attention
 from .projection import project_qkvg
+from . import variants
 from . import brute
 
 __all__ = ["gate_scores", "sigmoid", "gate_values", "sdpa", "gated_sdpa", "gated_decode",
            "gate_param_count", "sdpa_backward", "gated_sdpa_backward",
-           "gated_sdpa_backward_sampled", "first_token_attention", "project_qkvg", "brute"]
+           "gated_sdpa_backward_sampled", "first_token_attention", "project_qkvg", "variants", "brute"]

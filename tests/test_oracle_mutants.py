@@ -265,3 +265,61 @@ def test_unmutated_projection_copy_passes():
 @pytest.mark.parametrize("name", sorted(PROJ_MUTANTS))
 def test_projection_mutant_is_caught(name):
     assert not proj_pins_pass(load_proj_mutant(name))
+
+
+# --------------------------------------------------------------- gating variants
+VAR_SRC = os.path.join(os.path.dirname(SRC), "variants.py")
+VAR_MUTANTS = {
+    "ns_sigmoid_half_only": ("return 0.5 + 0.5 * sigmoid(Z)", "return 0.5 * sigmoid(Z)"),
+    "silu_without_input": ("return Z * sigmoid(Z)", "return sigmoid(Z)"),
+    "shared_over_dims_not_heads": ("return a.reshape(B, S, 1, D)", "return a.reshape(B, S, D, 1)"),
+    "rms_over_heads": ("np.mean(Y * Y, axis=-1, keepdims=True)", "np.mean(Y * Y, axis=-2, keepdims=True)"),
+    "additive_as_multiplicative": ("        return Y + g\n", "        return Y * g\n"),
+    "norm_after_gate": ("    if norm == \"rms\":\n        Y = rms_norm_heads(Y)\n", "    if norm == \"rms\":\n        Y = Y\n"),
+    "value_gate_uses_query_heads": ("return V * gate_layout(g, Hkv, D, mode)", "return V * gate_layout(g, Hkv, D, mode)[:, ::-1]"),
+}
+
+
+def load_var_mutant(name):
+    with open(VAR_SRC) as f:
+        src = f.read().replace("from .gated_sdpa import", "from oracle.gated_sdpa import")
+    if name is not None:
+        old, new = VAR_MUTANTS[name]
+        assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_var_mutant_{name}")
+    exec(compile(src, f"<variant mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def var_pins_pass(orc):
+    """Brute-force loops over the variant cases, and the G2 value gate by loops."""
+    from test_oracle_variants import CASES, brute_variant, draw, sig
+    try:
+        for mode, act, combine, norm in CASES:
+            B, S, Hq, Hkv, D, dm = 2, 4, 4, 2, 3, 4
+            N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+            t = draw(np.random.default_rng(11), B, S, Hq, Hkv, D, dm, N)
+            got = orc.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
+            if not np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12:
+                return False
+        t = draw(np.random.default_rng(12), 1, 4, 4, 2, 3, 4, 6)
+        Vg = orc.value_gate(t["X"], t["W"], t["V"], "elementwise")
+        for j in range(4):
+            for c in range(2):
+                for d in range(3):
+                    z = math.fsum(t["X"][0, j, k] * t["W"][k, c * 3 + d] for k in range(4))
+                    if abs(Vg[0, j, c, d] - t["V"][0, j, c, d] * sig(z)) > 1e-14:
+                        return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unmutated_variants_copy_passes():
+    assert var_pins_pass(load_var_mutant(None))
+
+
+@pytest.mark.parametrize("name", sorted(VAR_MUTANTS))
+def test_variants_mutant_is_caught(name):
+    assert not var_pins_pass(load_var_mutant(name))

@@ -1,0 +1,138 @@
+"""Pins of the gating-variant oracle (oracle.variants): brute-force loops,
+closed forms of the activations, and invariants between variants."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import variants as ov
+
+
+def draw(rng, B, S, Hq, Hkv, D, dm, N):
+    return dict(X=rng.standard_normal((B, S, dm)), W=rng.standard_normal((dm, N)) / math.sqrt(dm),
+                Q=rng.standard_normal((B, S, Hq, D)), K=rng.standard_normal((B, S, Hkv, D)),
+                V=rng.standard_normal((B, S, Hkv, D)))
+
+
+def sig(z):
+    return 1 / (1 + math.exp(-z)) if z >= 0 else math.exp(z) / (1 + math.exp(z))
+
+
+def brute_variant(t, mode, act, combine, norm):
+    """Pure-Python loops: SDPA row, optional RMSNorm, activation, combine."""
+    X, W, Q, K, V = (t[k] for k in "XWQKV")
+    B, S, Hq, D = Q.shape
+    G = Hq // K.shape[2]
+    dm = X.shape[2]
+    f = {"identity": lambda z: z, "sigmoid": sig, "ns_sigmoid": lambda z: 0.5 + 0.5 * sig(z),
+         "silu": lambda z: z * sig(z)}[act]
+    out = np.empty(Q.shape)
+    for b in range(B):
+        for i in range(S):
+            for h in range(Hq):
+                c = h // G
+                s = [math.fsum(Q[b, i, h, d] * K[b, j, c, d] for d in range(D)) / math.sqrt(D) for j in range(i + 1)]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = math.fsum(w)
+                y = [math.fsum(w[j] * V[b, j, c, d] for j in range(i + 1)) / tot for d in range(D)]
+                if norm == "rms":
+                    r = math.sqrt(math.fsum(v * v for v in y) / D + ov.RMS_EPS)
+                    y = [v / r for v in y]
+                for d in range(D):
+                    if mode == "none":
+                        out[b, i, h, d] = y[d]
+                        continue
+                    col = {"elementwise": h * D + d, "headwise": h, "shared": d}[mode]
+                    g = f(math.fsum(X[b, i, k] * W[k, col] for k in range(dm)))
+                    out[b, i, h, d] = y[d] * g if combine == "mul" else y[d] + g
+    return out
+
+
+CASES = [("elementwise", "ns_sigmoid", "mul", None), ("headwise", "sigmoid", "add", None),
+         ("elementwise", "silu", "add", None), ("shared", "sigmoid", "mul", None),
+         ("none", "sigmoid", "mul", "rms"), ("elementwise", "sigmoid", "mul", "rms"),
+         ("shared", "identity", "add", "rms"), ("headwise", "ns_sigmoid", "mul", "rms")]
+
+
+@pytest.mark.parametrize("mode,act,combine,norm", CASES)
+def test_matches_brute_force(mode, act, combine, norm):
+    B, S, Hq, Hkv, D, dm = 2, 5, 4, 2, 3, 4
+    N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+    t = draw(np.random.default_rng(len(mode) + len(act)), B, S, Hq, Hkv, D, dm, N)
+    got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
+    assert np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12
+
+
+def test_activation_closed_forms():
+    z = np.array([-40.0, -1.0, 0.0, 1.0, 40.0])
+    assert np.array_equal(ov.activation(z, "identity"), z)
+    ns = ov.activation(z, "ns_sigmoid")
+    assert ns[2] == 0.75 and ns[4] == 1.0 and abs(ns[0] - 0.5) <= 1e-17 and np.all((ns >= 0.5) & (ns <= 1))
+    si = ov.activation(z, "silu")
+    assert si[2] == 0.0 and si[4] == 40.0 and abs(si[0]) <= 40 * math.exp(-40) * 1.0001
+    assert abs(si[3] - 1 / (1 + math.exp(-1))) <= 1e-16 and abs(si[1] + math.exp(-1) / (1 + math.exp(-1))) <= 1e-16
+
+
+def test_default_variant_is_the_g1_oracle_bitwise():
+    t = draw(np.random.default_rng(1), 2, 9, 4, 2, 4, 6, 16)
+    a = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "elementwise")
+    b = oracle.gated_sdpa(t["X"], t["W"], t["Q"], t["K"], t["V"], "elementwise")
+    assert np.array_equal(a, b)
+
+
+def test_shared_equals_elementwise_with_tiled_weight():
+    rng = np.random.default_rng(2)
+    t = draw(rng, 1, 11, 4, 2, 4, 6, 4)
+    a = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "ns_sigmoid", "add")
+    Wt = np.tile(t["W"], (1, 4))                         # column h*D + d = column d, every head
+    b = ov.gated_sdpa_variant(t["X"], Wt, t["Q"], t["K"], t["V"], "elementwise", "ns_sigmoid", "add")
+    assert np.max(np.abs(a - b)) <= 1e-15
+
+
+def test_additive_with_zero_weight():
+    t = draw(np.random.default_rng(3), 1, 7, 2, 1, 4, 5, 8)
+    t["W"][:] = 0.0
+    Y = oracle.sdpa(t["Q"], t["K"], t["V"])
+    for act, const in [("sigmoid", 0.5), ("silu", 0.0), ("identity", 0.0), ("ns_sigmoid", 0.75)]:
+        got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "elementwise", act, "add")
+        assert np.array_equal(got, Y + const), act
+
+
+def test_rms_norm_gives_unit_rms_and_is_scale_free():
+    t = draw(np.random.default_rng(4), 2, 13, 4, 2, 8, 6, 1)
+    Yn = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "none", norm="rms")
+    Y = oracle.sdpa(t["Q"], t["K"], t["V"])
+    ms = np.mean(Y * Y, axis=-1)
+    rms = np.sqrt(np.mean(Yn * Yn, axis=-1))
+    assert np.max(np.abs(rms - np.sqrt(ms / (ms + ov.RMS_EPS)))) <= 1e-12 and np.all(rms <= 1)
+    Yn4 = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], 4 * t["V"], "none", norm="rms")
+    # only ε breaks scale freedom: the two differ by a factor within 1 ± ε/(2·ms)
+    bound = np.abs(Yn) * (ov.RMS_EPS / (2 * ms))[..., None] * 1.001 + 1e-15
+    assert np.all(np.abs(Yn4 - Yn) <= bound)
+    assert np.array_equal(np.sign(Yn), np.sign(Y))
+
+
+def test_value_gate_g2():
+    rng = np.random.default_rng(5)
+    B, S, Hq, Hkv, D, dm = 2, 10, 4, 2, 3, 5
+    t = draw(rng, B, S, Hq, Hkv, D, dm, Hkv * D)
+    Y = oracle.sdpa(t["Q"], t["K"], t["V"])
+    Wsat = np.zeros((dm, Hkv * D))
+    Xsat = np.zeros((B, S, dm))
+    Xsat[..., 0] = 1.0
+    Wsat[0, :] = 40.0                                    # logits +40: σ == 1.0 exactly
+    assert np.array_equal(ov.value_gated_sdpa(Xsat, Wsat, t["Q"], t["K"], t["V"], "elementwise"), Y)
+    W0 = np.zeros((dm, Hkv))                             # headwise, σ(0) = 1/2: SDPA is linear in V
+    assert np.max(np.abs(ov.value_gated_sdpa(t["X"], W0, t["Q"], t["K"], t["V"], "headwise") - Y / 2)) <= 1e-15
+    # brute force: gate each value row, then attend
+    got = ov.value_gated_sdpa(t["X"], t["W"], t["Q"], t["K"], t["V"], "elementwise")
+    Vg = np.empty_like(t["V"])
+    for b in range(B):
+        for j in range(S):
+            for c in range(Hkv):
+                for d in range(D):
+                    z = math.fsum(t["X"][b, j, k] * t["W"][k, c * D + d] for k in range(dm))
+                    Vg[b, j, c, d] = t["V"][b, j, c, d] * sig(z)
+    assert np.max(np.abs(got - oracle.sdpa(t["Q"], t["K"], Vg))) <= 1e-14
