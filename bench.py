@@ -10,6 +10,8 @@ kernel (the gated forward), timed per launch with HIP events on the stream it
 runs on; the decode workload (batch 64, one token against a 16384-long KV
 cache, 32/8 heads) as GB/s with its own roofline; the backward of the prefill
 path (gsa_backward) as TFLOP/s; the fused Q/K/V/gate projection as TFLOP/s;
+the gate design-space variants (activation, layout, combine, norm) as whole
+steps, and the G2 value gate as GB/s;
 the first-token attention diagnostic on the
 32k sink-mimicking workload as GB/s; and the fp64 oracle timed on the host
 cores on a bounded sample of the prefill workload.
@@ -38,11 +40,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-decode", action="store_true", help="skip the decode workload")
-    p.add_argument("--only", choices=["prefill", "decode", "backward", "diagnostic", "projection"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "backward", "diagnostic", "projection", "variants"], default=None,
                    help="run one workload's GPU part only (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     p.add_argument("--no-backward", action="store_true", help="skip the backward workload")
     p.add_argument("--no-projection", action="store_true", help="skip the fused input projection")
+    p.add_argument("--no-variants", action="store_true", help="skip the gate design-space variants")
     p.add_argument("--no-diagnostic", action="store_true",
                    help="skip the first-token attention diagnostic on the long_prefill workload")
     p.add_argument("--no-others", action="store_true",
@@ -247,6 +250,47 @@ def projection_bench(args, torch, gsa, cfg):
     }
 
 
+def variants_bench(args, torch, gsa, cfg):
+    """Design-space variants on the prefill workload, each timed as its whole step:
+    gate GEMM with the variant's activation, then gsa_forward_variant; and the
+    G2 value gate (gsa_value_gate, HBM-bound) as GB/s."""
+    from synth import make_inputs
+    inp = make_inputs(cfg, seed=0, device="cuda:0")
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    Y = torch.empty_like(Q)
+    out = {}
+    cases = [("elementwise", "sigmoid", "mul", None), ("elementwise", "ns_sigmoid", "mul", "rms"),
+             ("elementwise", "silu", "add", None), ("shared", "sigmoid", "mul", None)]
+    for layout, act, combine, norm in cases:
+        Wl = W if layout == "elementwise" else W[:, :cfg.D].contiguous()
+        G = torch.empty((cfg.B * cfg.S, Wl.shape[1]), dtype=torch.float32, device="cuda:0")
+
+        def step():
+            gsa.gate_logits(X, Wl, G=G, activation=act)
+            gsa.forward_variant(Q, K, V, G, layout, combine, norm, Y=Y)
+
+        ms, _, _ = time_steps(step, lambda: None, args.steps, args.warmup, torch)
+        flops = cfg.attention_flops() + 2 * cfg.B * cfg.S * cfg.d_model * Wl.shape[1]
+        out[f"{layout}/{act}/{combine}/{norm or 'no-norm'}"] = {
+            "ms_per_step": ms, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "flops_per_step": flops}
+    Nv = cfg.Hkv * cfg.D
+    Gv = torch.rand((cfg.B * cfg.S, Nv), dtype=torch.float32, device="cuda:0")
+    Vo = torch.empty_like(V)
+
+    def vstep():
+        gsa.value_gate(V, Gv, "elementwise", Vout=Vo)
+
+    ms, _, _ = time_steps(vstep, lambda: None, args.steps, args.warmup, torch)
+    nbytes = 2 * V.numel() * V.element_size() + Gv.numel() * 4
+    out["value_gate_elementwise"] = {
+        "ms_per_step": ms, "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+        "roofline": {"kernel": "value_gate_kernel", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes}}
+    return {"workload": cfg.name, "cases": out}
+
+
 def diagnostic_bench(args, torch, gsa, cfg):
     """gsa_first_token_attention (F = exp(q_i·k_0/√D − LSE_i) per head and row, plus
     per-head means) on the long_prefill workload, whose token-0 keys are scaled ×8
@@ -350,6 +394,9 @@ def main():
     pcfg = CONFIGS["dense_prefill"]
     dcfg = CONFIGS["decode"]
     out = None
+    if args.only == "variants":
+        print(json.dumps(variants_bench(args, torch, gsa, pcfg)), flush=True)
+        return
     if args.only == "projection":
         pj = projection_bench(args, torch, gsa, pcfg)
         print(json.dumps(dict(pj, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
@@ -407,6 +454,12 @@ def main():
         print(f"# projection: {pj['ms_per_step']*1e3:.1f} us, {pj['value']:.0f} TFLOP/s", file=sys.stderr,
               flush=True)
         out["projection"] = pj
+    if out is not None and not args.no_variants and args.only is None:
+        vr = variants_bench(args, torch, gsa, pcfg)
+        torch.cuda.empty_cache()
+        print("# variants: " + ", ".join(f"{k} {v['value']:.0f} {v['unit']}" for k, v in vr["cases"].items()),
+              file=sys.stderr, flush=True)
+        out["variants"] = vr
     if out is not None and not args.no_diagnostic and args.only is None:
         dg = diagnostic_bench(args, torch, gsa, CONFIGS["long_prefill"])
         torch.cuda.empty_cache()

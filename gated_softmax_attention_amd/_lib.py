@@ -19,6 +19,17 @@ GSA_BF16 = 1
 GSA_GATE_NONE = 0
 GSA_GATE_ELEMENTWISE = 1
 GSA_GATE_HEADWISE = 2
+GSA_GATE_SHARED = 3
+
+GSA_ACT_IDENTITY = 0
+GSA_ACT_SIGMOID = 1
+GSA_ACT_NS_SIGMOID = 2
+GSA_ACT_SILU = 3
+
+GSA_COMBINE_MUL = 0
+GSA_COMBINE_ADD = 1
+GSA_NORM_NONE = 0
+GSA_NORM_RMS = 1
 
 # name -> (restype, argtypes); the exported surface of include/gsa.h
 _P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -34,6 +45,8 @@ SIGNATURES = {
     "gsa_decode": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
     "gsa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64, _I]),
     "gsa_backward": (_I, [_P] * 14 + [_I64] * 6 + [_I, _I, _P, _SZ, _P]),
+    "gsa_forward_variant": (_I, [_P] * 6 + [_I64] * 5 + [_I, _I, _I, _I, _P]),
+    "gsa_value_gate": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_project_qkvg": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P]),
     "gsa_first_token_attention": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
 }

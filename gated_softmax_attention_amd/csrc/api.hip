@@ -14,7 +14,7 @@
 
 namespace gsa {
 hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, int64_t K, int64_t N,
-                            bool bf16_inputs, bool apply_sigmoid, hipStream_t stream);
+                            bool bf16_inputs, int act, hipStream_t stream);
 hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const float* G, void* Y,
                            float* Lse, int B, int S, int Skv, int Hq, int Hkv, int D, int mode,
                            bool bf16_inputs, hipStream_t stream);
@@ -30,6 +30,11 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const vo
 int bwd_kv_slices(int B, int S, int Hq, int Hkv);
 hipError_t launch_project_qkvg(const void* X, const void* W, void* Q, void* Kp, void* V, float* G, int64_t M,
                                int64_t K, int64_t nq, int64_t nkv, int64_t ng, hipStream_t stream);
+hipError_t launch_attn_fwd_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                                   float* Lse, int B, int S, int Hq, int Hkv, int D, int layout, int add,
+                                   int rms, bool bf16_inputs, hipStream_t stream);
+hipError_t launch_value_gate(const void* V, const float* G, void* Vout, int64_t rows, int Hkv, int D,
+                             bool headwise, bool bf16_inputs, hipStream_t st);
 hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 int bwd_stat_rows(int S);
@@ -152,14 +157,14 @@ const char* gsa_status_string(int status) {
 const char* gsa_last_error_message(void) { return g_last_error.c_str(); }
 
 gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, int64_t d_model,
-                           int64_t N, int dtype, int apply_sigmoid, void* stream) {
+                           int64_t N, int dtype, int activation, void* stream) {
   if (!X || !W || !G) return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: null pointer");
   if (M <= 0 || d_model <= 0 || N <= 0)
     return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: sizes must be positive (M=%lld d_model=%lld N=%lld)",
                 (long long)M, (long long)d_model, (long long)N);
   if (gsa_status st = check_dtype("gsa_gate_logits", dtype)) return st;
-  if (apply_sigmoid != 0 && apply_sigmoid != 1)
-    return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: apply_sigmoid must be 0 or 1");
+  if (activation < GSA_ACT_IDENTITY || activation > GSA_ACT_SILU)
+    return fail(GSA_ERR_INVALID_ARG, "gsa_gate_logits: activation %d is not a gsa_activation", activation);
   if (d_model % 8 != 0)
     return fail(GSA_ERR_UNSUPPORTED, "gsa_gate_logits: d_model=%lld is not a multiple of 8",
                 (long long)d_model);
@@ -168,7 +173,7 @@ gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, in
   if (!aligned16(X) || !aligned16(W) || !aligned16(G))
     return fail(GSA_ERR_MISALIGNED, "gsa_gate_logits: X, W and G must be 16-byte aligned");
   if (gsa_status st = check_device()) return st;
-  return hip_result(gsa::launch_gate_gemm(X, W, G, M, d_model, N, dtype == GSA_BF16, apply_sigmoid == 1,
+  return hip_result(gsa::launch_gate_gemm(X, W, G, M, d_model, N, dtype == GSA_BF16, activation,
                                           (hipStream_t)stream),
                     "gsa_gate_logits launch");
 }
@@ -375,6 +380,51 @@ gsa_status gsa_project_qkvg(const void* X, const void* W, void* Q, void* K, void
     return fail(GSA_ERR_MISALIGNED, "%s: X, W, Q, K, V and G must be 16-byte aligned", fn);
   if (gsa_status st = check_device()) return st;
   return hip_result(gsa::launch_project_qkvg(X, W, Q, K, V, G, M, d_model, nq, nkv, n_gate, (hipStream_t)stream),
+                    fn);
+}
+
+gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                               float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                               int layout, int combine, int norm, int dtype, void* stream) {
+  const char* fn = "gsa_forward_variant";
+  if (!Q || !K || !V || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (layout < GSA_GATE_NONE || layout > GSA_GATE_SHARED)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown gate layout %d", fn, layout);
+  if (combine != GSA_COMBINE_MUL && combine != GSA_COMBINE_ADD)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown combine %d", fn, combine);
+  if (norm != GSA_NORM_NONE && norm != GSA_NORM_RMS)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown norm %d", fn, norm);
+  // the shape rules of gsa_forward, with the shared layout checked as a gate
+  if (gsa_status st = check_attn_shape(fn, B, S, Hq, Hkv, D, layout == GSA_GATE_SHARED ? GSA_GATE_ELEMENTWISE
+                                                                                        : layout, G))
+    return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "%s: Q, K, V, G and Y must be 16-byte aligned", fn);
+  if (LSE && ((uintptr_t)LSE % 4) != 0) return fail(GSA_ERR_MISALIGNED, "%s: LSE must be 4-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_attn_fwd_variant(Q, K, V, G, Y, LSE, (int)B, (int)S, (int)Hq, (int)Hkv, (int)D,
+                                                 layout, combine == GSA_COMBINE_ADD, norm == GSA_NORM_RMS,
+                                                 dtype == GSA_BF16, (hipStream_t)stream),
+                    fn);
+}
+
+gsa_status gsa_value_gate(const void* V, const float* G, void* Vout, int64_t B, int64_t S, int64_t Hkv,
+                          int64_t D, int layout, int dtype, void* stream) {
+  const char* fn = "gsa_value_gate";
+  if (!V || !G || !Vout) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B <= 0 || S <= 0 || Hkv <= 0 || D <= 0) return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+  if (layout != GSA_GATE_ELEMENTWISE && layout != GSA_GATE_HEADWISE)
+    return fail(GSA_ERR_INVALID_ARG, "%s: layout must be GSA_GATE_ELEMENTWISE or GSA_GATE_HEADWISE", fn);
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (D != 64 && D != 128) return fail(GSA_ERR_UNSUPPORTED, "%s: head dim %lld is not 64 or 128", fn, (long long)D);
+  if (B * S > kIntMax || B * S * Hkv * D > ((int64_t)1 << 40))
+    return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  if (!aligned16(V) || !aligned16(G) || !aligned16(Vout))
+    return fail(GSA_ERR_MISALIGNED, "%s: V, G and Vout must be 16-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_value_gate(V, G, Vout, B * S, (int)Hkv, (int)D, layout == GSA_GATE_HEADWISE,
+                                           dtype == GSA_BF16, (hipStream_t)stream),
                     fn);
 }
 

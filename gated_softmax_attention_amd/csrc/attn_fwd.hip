@@ -44,7 +44,28 @@ constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 }  // namespace fwd
 
-enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2 };
+enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2, kGateVariant = 3 };
+
+// Epilogue of the design-space variants (MODE == kGateVariant only): the gate
+// layout (0 none, 1 elementwise column h·D + d, 2 headwise column h, 3 shared
+// column d for every head), additive instead of multiplicative combination,
+// and a per-head RMSNorm (unit weight, ε = 1e-6) of the SDPA output first.
+// The gate values G arrive already activated (gsa_gate_logits' activation).
+struct FwdEpi {
+  int layout, add, rms;
+};
+constexpr float kRmsEps = 1e-6f;
+
+// the gate value of (row tok, head, dim d) for a variant layout
+__device__ __forceinline__ float variant_gate(const float* __restrict__ Gate, const FwdEpi& ep, int64_t tok,
+                                              int Hq, int D, int head, int d) {
+  if (ep.layout == kGateElem) return Gate[(tok * Hq + head) * D + d];
+  if (ep.layout == kGateHead) return Gate[tok * Hq + head];
+  return Gate[tok * D + d];
+}
+__device__ __forceinline__ float variant_combine(float y, float g, const FwdEpi& ep) {
+  return ep.add ? y + g : y * g;
+}
 
 #ifndef GSA_FWD_QB
 #define GSA_FWD_QB 1
@@ -57,7 +78,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1)
 void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                           const bf16* __restrict__ V, const float* __restrict__ Gate,
                           bf16* __restrict__ Y, float* __restrict__ Lse, int B, int S, int Hq,
-                          int Hkv, int n_qtiles, float scale_log2) {
+                          int Hkv, int n_qtiles, float scale_log2, FwdEpi ep) {
   using namespace fwd;
   constexpr int BMQ = BM * QB;    // query rows per workgroup (QB blocks of 32 per wave)
   constexpr int CH = D / 8;       // 16-byte chunks per K/V row
@@ -410,6 +431,37 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const float inv = 1.0f / l_tot;
     const int64_t tok = (int64_t)b * S + my_q[qb];
     bf16* yrow = Y + tok * q_row + (int64_t)head * D;
+    if constexpr (MODE == kGateVariant) {
+      // the row's D values sit in this lane (half) and in lane ^ 32 (other half)
+      float rn = 1.0f;
+      if (ep.rms) {
+        float ss = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = o[qb][dt][r] * inv;
+            ss = fmaf(y, y, ss);
+          }
+        ss += __shfl_xor(ss, 32);   // lane ^ 32 holds the same row (same my_q: both take this path)
+        rn = 1.0f / sqrtf(ss / (float)D + kRmsEps);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = dt * 32 + 8 * i + 4 * hl;
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            y[j] = o[qb][dt][4 * i + j] * inv * rn;
+            if (ep.layout != kGateNone)
+              y[j] = variant_combine(y[j], variant_gate(Gate, ep, tok, Hq, D, head, d0 + j), ep);
+          }
+          *(u32x2*)(yrow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+      continue;
+    }
     float gh = 1.0f;
     if constexpr (MODE == kGateHead) gh = Gate[tok * Hq + head];
 #pragma unroll
@@ -441,7 +493,7 @@ __global__ __launch_bounds__(256)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, const float* __restrict__ Gate,
                          float* __restrict__ Y, float* __restrict__ Lse, int B, int S, int Skv,
-                         int Hq, int Hkv, int n_qtiles, float scale_log2) {
+                         int Hq, int Hkv, int n_qtiles, float scale_log2, FwdEpi ep) {
   constexpr int BMF = 64, BNF = 32, DPL = D / 4, LDF = D + 4;
   __shared__ float Ks[BNF * LDF];
   __shared__ float Vs[BNF * LDF];
@@ -507,11 +559,31 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     }
     __syncthreads();
   }
+  // (a row's 4 lanes are adjacent and share q: they leave together)
   if (q >= S) return;
   const float inv = 1.0f / l_run;
   if (Lse != nullptr && part == 0)
     Lse[((int64_t)b * Hq + head) * S + q] = (m_run + log2f(l_run)) * kLn2;
   const int64_t tok = (int64_t)b * S + q;
+  if constexpr (MODE == kGateVariant) {
+    float rn = 1.0f;
+    if (ep.rms) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ss = fmaf(acc[e] * inv, acc[e] * inv, ss);
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      rn = 1.0f / sqrtf(ss / (float)D + kRmsEps);
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const int d = part * DPL + e;
+      float y = acc[e] * inv * rn;
+      if (ep.layout != kGateNone) y = variant_combine(y, variant_gate(Gate, ep, tok, Hq, D, head, d), ep);
+      Y[tok * q_row + (int64_t)head * D + d] = y;
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
     const int d = part * DPL + e;
@@ -524,23 +596,24 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 
 template <int D, int MODE, int QB = GSA_FWD_QB>
 static void launch_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
-                        float* Lse, int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st) {
+                        float* Lse, int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st,
+                        FwdEpi ep = FwdEpi{0, 0, 0}) {
   const int nq = ceil_div(S, fwd::BM * QB);
   const int64_t blocks = (int64_t)nq * Hq * B;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE, QB>), dim3((unsigned)blocks), dim3(256), 0, st,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, Lse, B, S, Hq,
-                     Hkv, nq, scale_log2);
+                     Hkv, nq, scale_log2, ep);
 }
 
 template <int D, int MODE>
 static void launch_f32(const void* Q, const void* K, const void* V, const float* G, void* Y,
                        float* Lse, int B, int S, int Skv, int Hq, int Hkv, float scale_log2,
-                       hipStream_t st) {
+                       hipStream_t st, FwdEpi ep = FwdEpi{0, 0, 0}) {
   const int nq = ceil_div(S, 64);
   const int64_t blocks = (int64_t)nq * Hq * B;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, MODE>), dim3((unsigned)blocks), dim3(256), 0, st,
                      (const float*)Q, (const float*)K, (const float*)V, G, (float*)Y, Lse, B, S,
-                     Skv, Hq, Hkv, nq, scale_log2);
+                     Skv, Hq, Hkv, nq, scale_log2, ep);
 }
 
 template <int D>
@@ -567,6 +640,24 @@ hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const fl
     dispatch_mode<128>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
   else
     dispatch_mode<64>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
+  return hipGetLastError();
+}
+
+// The design-space variants (prefill): the gate layout (kGateNone, kGateElem,
+// kGateHead or 3 = shared), additive combination and per-head RMSNorm, on the
+// same main loop as launch_attn_fwd.
+hipError_t launch_attn_fwd_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                                   float* Lse, int B, int S, int Hq, int Hkv, int D, int layout, int add,
+                                   int rms, bool bf16_inputs, hipStream_t stream) {
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  const FwdEpi ep{layout, add, rms};
+  if (bf16_inputs) {
+    if (D == 128) launch_bf16<128, kGateVariant>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, stream, ep);
+    else launch_bf16<64, kGateVariant>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, stream, ep);
+  } else {
+    if (D == 128) launch_f32<128, kGateVariant>(Q, K, V, G, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream, ep);
+    else launch_f32<64, kGateVariant>(Q, K, V, G, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream, ep);
+  }
   return hipGetLastError();
 }
 

@@ -45,6 +45,17 @@ __device__ __forceinline__ float sigmoidf(float z) {
   return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Gate activations ("GatedAttention [2025]" §1.2.2 item (5); NS-sigmoid of
+// §1.4.2 (iv)): 0 identity (the raw logits), 1 sigmoid, 2 NS-sigmoid
+// 0.5 + 0.5·σ(z), 3 SiLU z·σ(z).
+enum : int { kActIdentity = 0, kActSigmoid = 1, kActNsSigmoid = 2, kActSilu = 3 };
+__device__ __forceinline__ float gate_act(float z, int act) {
+  if (act == kActSigmoid) return sigmoidf(z);
+  if (act == kActNsSigmoid) return fmaf(0.5f, sigmoidf(z), 0.5f);
+  if (act == kActSilu) return z * sigmoidf(z);
+  return z;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -1,4 +1,5 @@
-// Gate projection with fused sigmoid: G = σ(X·W_θ)  (bias-free).
+// Gate projection with fused activation: G = act(X·W_θ)  (bias-free; act is the
+// sigmoid by default, or the identity, NS-sigmoid or SiLU: gate_act in common.h).
 //
 // Source: "GatedAttention [2025]" page, §1.2.2 gating equation Y' = Y ⊙ σ(X W_θ)
 // with σ the logistic sigmoid (default activation, same section); the bias-free
@@ -25,7 +26,7 @@ constexpr int LD = BK + 8;  // LDS row stride in bf16 (144 B: 16-B aligned, rota
 __global__ __launch_bounds__(256, 2)
 void gate_gemm_bf16_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                            float* __restrict__ G, int M, int K, int N, int tiles_n,
-                           int apply_sigmoid) {
+                           int act) {
   using namespace gemm;
   __shared__ __align__(16) bf16 As[2][BM * LD];
   __shared__ __align__(16) bf16 Bs[2][BN * LD];
@@ -132,7 +133,7 @@ void gate_gemm_bf16_kernel(const bf16* __restrict__ X, const bf16* __restrict__ 
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         if (m < M && n < N) {
           const float z = acc[i][j][r];
-          G[m * N + n] = apply_sigmoid ? sigmoidf(z) : z;
+          G[m * N + n] = gate_act(z, act);
         }
       }
     }
@@ -174,7 +175,7 @@ template <bool ROUTE>
 __global__ __launch_bounds__(512, 1)
 void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                                float* __restrict__ G, int M, int K, int N, int tiles_m, int tiles_n,
-                               int apply_sigmoid, ProjOut po) {
+                               int act, ProjOut po) {
   using namespace gemm_big;
   __shared__ __align__(16) bf16 Xs[2][BM * XSL * 8];
   __shared__ __align__(16) bf16 Ws[2][BK * WSL * 8];
@@ -339,7 +340,7 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
         for (int r = 0; r < 16; ++r) {
           const int m = mb + 8 * (r >> 2) + (r & 3);
           const float z = acc[mt][nt][r];
-          const float v = apply_sigmoid ? sigmoidf(z) : z;
+          const float v = gate_act(z, act);
           if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
         }
       }
@@ -403,7 +404,7 @@ constexpr uint32_t kOOB = 0xfffffff0u;
 __global__ __launch_bounds__(256)
 void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                                   float* __restrict__ G, int M, int K, int N, int tiles_n,
-                                  int apply_sigmoid) {
+                                  int act) {
   using namespace gemm_narrow;
   __shared__ __align__(16) bf16 Xs[WAVES][NS][XSLOTS * 8];
   __shared__ __align__(16) bf16 Ws[WAVES][NS][WSLOTS * 8];
@@ -505,7 +506,7 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-    if (m < M && n < N) G[(int64_t)m * N + n] = apply_sigmoid ? sigmoidf(acc[r]) : acc[r];
+    if (m < M && n < N) G[(int64_t)m * N + n] = gate_act(acc[r], act);
   }
 }
 
@@ -513,7 +514,7 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
 __global__ __launch_bounds__(256)
 void gate_gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__ W,
                           float* __restrict__ G, int M, int K, int N, int tiles_n,
-                          int apply_sigmoid) {
+                          int act) {
   constexpr int T = 64, TK = 16;
   __shared__ float As[TK][T + 4];
   __shared__ float Bs[TK][T + 4];
@@ -551,37 +552,37 @@ void gate_gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__
     for (int j = 0; j < 4; ++j) {
       const int64_t m = m0 + ty * 4 + i;
       const int n = n0 + tx * 4 + j;
-      if (m < M && n < N) G[m * N + n] = apply_sigmoid ? sigmoidf(acc[i][j]) : acc[i][j];
+      if (m < M && n < N) G[m * N + n] = gate_act(acc[i][j], act);
     }
 }
 
 hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, int64_t K, int64_t N,
-                            bool bf16_inputs, bool apply_sigmoid, hipStream_t stream) {
+                            bool bf16_inputs, int act, hipStream_t stream) {
   if (bf16_inputs && M >= 256 && N >= 256 && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) &&
       K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, gemm_big::BN);
     const int tiles_m = (int)ceil_div<int64_t>(M, gemm_big::BM);
     hipLaunchKernelGGL(gate_gemm_bf16_big_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_m, tiles_n,
-                       (int)apply_sigmoid, ProjOut{nullptr, nullptr, nullptr, 0, 0});
+                       act, ProjOut{nullptr, nullptr, nullptr, 0, 0});
   } else if (bf16_inputs && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) && K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, 32);
     const int64_t tiles = ceil_div<int64_t>(M, 32) * tiles_n;
     hipLaunchKernelGGL(gate_gemm_bf16_narrow_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_n,
-                       (int)apply_sigmoid);
+                       act);
   } else if (bf16_inputs) {
     const int tiles_n = (int)ceil_div<int64_t>(N, gemm::BN);
     const int64_t tiles = ceil_div<int64_t>(M, gemm::BM) * tiles_n;
     hipLaunchKernelGGL(gate_gemm_bf16_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_n,
-                       (int)apply_sigmoid);
+                       act);
   } else {
     const int tiles_n = (int)ceil_div<int64_t>(N, 64);
     const int64_t tiles = ceil_div<int64_t>(M, 64) * tiles_n;
     hipLaunchKernelGGL(gate_gemm_f32_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        (const float*)X, (const float*)W, G, (int)M, (int)K, (int)N, tiles_n,
-                       (int)apply_sigmoid);
+                       act);
   }
   return hipGetLastError();
 }

@@ -34,8 +34,14 @@ def _dtype(*ts):
     return _DTYPES[dt]
 
 
-def gate_logits(X, W, G=None, apply_sigmoid=True, stream=None):
+ACTIVATIONS = {"identity": _lib.GSA_ACT_IDENTITY, "sigmoid": _lib.GSA_ACT_SIGMOID,
+               "ns_sigmoid": _lib.GSA_ACT_NS_SIGMOID, "silu": _lib.GSA_ACT_SILU}
+
+
+def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, stream=None):
     """G = σ(X·W_θ) (or the logits Z when apply_sigmoid is False), float32 [M, N].
+    ``activation`` ("identity", "sigmoid", "ns_sigmoid", "silu") overrides
+    apply_sigmoid.
 
     X: [..., d_model] (leading dims flattened to M rows); W: [d_model, N].
     """
@@ -49,8 +55,14 @@ def gate_logits(X, W, G=None, apply_sigmoid=True, stream=None):
     elif G.dtype != torch.float32 or G.numel() != M * N:
         raise ValueError("G must be float32 with M*N elements")
     lib = _lib.load()
+    if activation is None:
+        act = _lib.GSA_ACT_SIGMOID if apply_sigmoid else _lib.GSA_ACT_IDENTITY
+    elif activation in ACTIVATIONS:
+        act = ACTIVATIONS[activation]
+    else:
+        raise ValueError(f"activation must be one of {list(ACTIVATIONS)}")
     _lib.check(lib.gsa_gate_logits(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N,
-                                   _dtype(X, W), int(bool(apply_sigmoid)), _stream(stream)))
+                                   _dtype(X, W), act, _stream(stream)))
     return G
 
 
@@ -165,6 +177,43 @@ def backward(X, W, G, Q, K, V, Y, LSE, dY, mode, workspace=None, stream=None):
         _dev(dV, "dV"), B, S, Hq, Hkv, D, d_model, _mode(mode), _dtype(Q, K, V, Y, dY),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
     return {"dQ": dQ, "dK": dK, "dV": dV, "dX": dX, "dW": dW}
+
+
+LAYOUTS = {"none": _lib.GSA_GATE_NONE, "elementwise": _lib.GSA_GATE_ELEMENTWISE,
+           "headwise": _lib.GSA_GATE_HEADWISE, "shared": _lib.GSA_GATE_SHARED}
+
+
+def forward_variant(Q, K, V, G, layout, combine="mul", norm=None, Y=None, LSE=None, stream=None):
+    """Causal SDPA with a design-space gate: combine(norm(Y), G) with G already
+    activated (gate_logits' activation), layout in LAYOUTS, combine "mul" or
+    "add", norm None or "rms".  Returns Y' (and LSE when an LSE tensor is given)."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
+    if layout not in LAYOUTS or combine not in ("mul", "add") or norm not in (None, "rms"):
+        raise ValueError("layout, combine or norm not recognised")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    lib = _lib.load()
+    _lib.check(lib.gsa_forward_variant(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), None if G is None else _dev(G, "G"), _dev(Y, "Y"),
+        None if LSE is None else _dev(LSE, "LSE"), B, S, Hq, Hkv, D, LAYOUTS[layout],
+        _lib.GSA_COMBINE_ADD if combine == "add" else _lib.GSA_COMBINE_MUL,
+        _lib.GSA_NORM_RMS if norm == "rms" else _lib.GSA_NORM_NONE, _dtype(Q, K, V, Y), _stream(stream)))
+    return Y if LSE is None else (Y, LSE)
+
+
+def value_gate(V, G, layout, Vout=None, stream=None):
+    """G2: V ⊙ G per key/value head (elementwise G [B*S, Hkv*D]) or per head
+    (headwise G [B*S, Hkv]); returns the gated values, V's shape and dtype."""
+    B, S, Hkv, D = V.shape
+    if Vout is None:
+        Vout = torch.empty_like(V)
+    lib = _lib.load()
+    _lib.check(lib.gsa_value_gate(_dev(V, "V"), _dev(G, "G"), _dev(Vout, "Vout"), B, S, Hkv, D,
+                                  LAYOUTS[layout], _dtype(V, Vout), _stream(stream)))
+    return Vout
 
 
 def project_qkvg(X, Wcat, Hq, Hkv, D, n_gate, stream=None):

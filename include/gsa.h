@@ -54,8 +54,26 @@ typedef enum gsa_dtype { GSA_FP32 = 0, GSA_BF16 = 1 } gsa_dtype;
 typedef enum gsa_gate_mode {
   GSA_GATE_NONE = 0,         /* plain causal SDPA, no gate (G must be NULL) */
   GSA_GATE_ELEMENTWISE = 1,  /* G is [rows, Hq*D]; column h*D + d gates head h, dim d */
-  GSA_GATE_HEADWISE = 2      /* G is [rows, Hq];   column h gates all of head h       */
+  GSA_GATE_HEADWISE = 2,     /* G is [rows, Hq];   column h gates all of head h       */
+  GSA_GATE_SHARED = 3        /* G is [rows, D];    column d gates dim d of every head
+                                (gsa_forward_variant only) */
 } gsa_gate_mode;
+
+/* Gate activation applied by gsa_gate_logits ("GatedAttention [2025]" §1.2.2
+   item (5); NS-sigmoid from §1.4.2 (iv)). */
+typedef enum gsa_activation {
+  GSA_ACT_IDENTITY = 0,      /* the raw logits Z = X·W_θ */
+  GSA_ACT_SIGMOID = 1,       /* σ(Z) = 1 / (1 + e^{-Z}) (the default) */
+  GSA_ACT_NS_SIGMOID = 2,    /* 0.5 + 0.5·σ(Z), range [0.5, 1] */
+  GSA_ACT_SILU = 3           /* Z·σ(Z) */
+} gsa_activation;
+
+/* How gsa_forward_variant applies the gate ("GatedAttention [2025]" §1.2.2 item (4)). */
+typedef enum gsa_combine { GSA_COMBINE_MUL = 0, GSA_COMBINE_ADD = 1 } gsa_combine;
+
+/* Optional per-head normalisation of the SDPA output before the gate
+   ("GatedAttention [2025]" §1.4.1, Table 3 row 5). */
+typedef enum gsa_norm { GSA_NORM_NONE = 0, GSA_NORM_RMS = 1 } gsa_norm;
 
 /* Library version, encoded as major*10000 + minor*100 + patch. */
 int gsa_version(void);
@@ -67,18 +85,19 @@ const char* gsa_status_string(int status);
 const char* gsa_last_error_message(void);
 
 /*
- * Gate projection with fused sigmoid: G = σ(X·W_θ) ("GatedAttention [2025]"
+ * Gate projection with fused activation: G = act(X·W_θ) ("GatedAttention [2025]"
  * §1.2.2 gating equation; no bias, as the §3.2 snippet on "10 · 门控" has
  * bias=False).
  *   X : [M, d_model] of dtype   (M = B*S token rows, the hidden states after pre-norm)
- *   W : [d_model, N] of dtype   (N = Hq*D elementwise, Hq headwise)
+ *   W : [d_model, N] of dtype   (N = Hq*D elementwise, Hq headwise, D shared)
  *   G : [M, N] float32 output
- *   apply_sigmoid: 1 stores σ(Z), 0 stores the raw logits Z = X·W_θ.
+ *   activation: a gsa_activation; GSA_ACT_SIGMOID (1) stores σ(Z), the G1
+ *     gate; GSA_ACT_IDENTITY (0) stores the raw logits Z = X·W_θ.
  * Requires d_model % 8 == 0.  Sizes must be positive.
  */
 gsa_status gsa_gate_logits(const void* X, const void* W, float* G,
                            int64_t M, int64_t d_model, int64_t N,
-                           int dtype, int apply_sigmoid, void* stream);
+                           int dtype, int activation, void* stream);
 
 /*
  * Causal gated SDPA forward (prefill): for every batch b, query head h and
@@ -175,6 +194,38 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
                         float* dW, void* dQ, void* dK, void* dV, int64_t B, int64_t S, int64_t Hq,
                         int64_t Hkv, int64_t D, int64_t d_model, int mode, int dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * gsa_forward for the other points of the gate design space ("GatedAttention
+ * [2025]" §1.2.2 items (3)-(5) and §1.4.1):
+ *   Y'[b,i,h,:] = combine(norm(Y[b,i,h,:]), gate)
+ * with Y the causal SDPA output (gsa_forward's definition), norm the identity
+ * or a per-head RMSNorm over the D values (unit weight, ε = 1e-6), and
+ * combine Y ⊙ g (GSA_COMBINE_MUL) or Y + g (GSA_COMBINE_ADD).  The gate values
+ * g are G as given (already activated by gsa_gate_logits):
+ *   layout GSA_GATE_ELEMENTWISE: G [B*S, Hq*D], column h*D + d
+ *          GSA_GATE_HEADWISE:    G [B*S, Hq],   column h
+ *          GSA_GATE_SHARED:      G [B*S, D],    column d for every head
+ *          GSA_GATE_NONE:        G NULL: Y' = norm(Y)
+ *   LSE: optional ([B, Hq, S] float32, as gsa_forward_lse; NULL skips it).
+ * Other arguments and rules as gsa_forward.
+ */
+gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                               float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                               int layout, int combine, int norm, int dtype, void* stream);
+
+/*
+ * G2 value gating ("GatedAttention [2025]" §1.2.2, position G2): the gate
+ * scales the value map before attention,
+ *   Vout[t, c, d] = V[t, c, d] · G[t, c*D + d]   (GSA_GATE_ELEMENTWISE)
+ *   Vout[t, c, d] = V[t, c, d] · G[t, c]         (GSA_GATE_HEADWISE)
+ * for token rows t < B*S and key/value heads c; gsa_forward with mode
+ * GSA_GATE_NONE on Vout then gives the G2-gated attention.
+ *   V, Vout : [B, S, Hkv, D] of dtype (may not overlap)   G : float32 from
+ *   gsa_gate_logits (σ of X·W_v).  D in {64, 128}; pointers 16-byte aligned.
+ */
+gsa_status gsa_value_gate(const void* V, const float* G, void* Vout, int64_t B, int64_t S, int64_t Hkv,
+                          int64_t D, int layout, int dtype, void* stream);
 
 /*
  * Fused input projection: Q, K, V and the gate from one pass over X,

@@ -67,16 +67,21 @@ def rms_norm_heads(Y, eps=RMS_EPS):
     return Y / np.sqrt(np.mean(Y * Y, axis=-1, keepdims=True) + eps)
 
 
-def gated_sdpa_variant(X, W, Q, K, V, mode, act="sigmoid", combine="mul", norm=None):
+def gated_sdpa_variant(X, W, Q, K, V, mode, act="sigmoid", combine="mul", norm=None, rows=None):
     """Y' for one point of the G1 design space (float64).
 
     mode in {"none", "elementwise", "headwise", "shared"}; act in ACTIVATIONS;
     combine in {"mul", "add"}; norm in {None, "rms"}.  With mode "none" the
-    result is the (optionally normalised) SDPA output.
+    result is the (optionally normalised) SDPA output.  With ``rows`` only
+    those query rows are evaluated and returned ([B, len(rows), Hq, D]).
     """
     Q = np.asarray(Q, dtype=np.float64)
     B, S, Hq, D = Q.shape
-    Y = sdpa(Q, K, V)
+    Y = sdpa(Q, K, V, rows=rows)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        Y = Y[:, rows]
+        X = np.asarray(X, dtype=np.float64)[:, rows] if X is not None else None
     if norm == "rms":
         Y = rms_norm_heads(Y)
     elif norm is not None:

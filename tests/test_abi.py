@@ -87,7 +87,8 @@ def test_gate_logits_argument_checks(lib):
     assert gl(X=None) == _lib.GSA_ERR_INVALID_ARG
     assert gl(M=0) == _lib.GSA_ERR_INVALID_ARG
     assert gl(N=-1) == _lib.GSA_ERR_INVALID_ARG
-    assert gl(sig=2) == _lib.GSA_ERR_INVALID_ARG
+    assert gl(sig=4) == _lib.GSA_ERR_INVALID_ARG          # not a gsa_activation
+    assert gl(sig=-1) == _lib.GSA_ERR_INVALID_ARG
     assert gl(dt=3) == _lib.GSA_ERR_UNSUPPORTED
     assert gl(dm=60) == _lib.GSA_ERR_UNSUPPORTED
     assert gl(W=MIS) == _lib.GSA_ERR_MISALIGNED
@@ -177,6 +178,35 @@ def test_backward_workspace_arithmetic(lib):
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, 3, D, 64, 1) == 0
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 0, 1) == 0
     assert lib.gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, 64, 9) == 0
+
+
+def test_forward_variant_argument_checks(lib):
+    def fv(Q=FAKE, G=FAKE, Y=FAKE, LSE=None, B=1, S=8, Hq=4, Hkv=2, D=128, layout=3, comb=0, norm=1, dtype=1):
+        return lib.gsa_forward_variant(Q, FAKE, FAKE, G, Y, LSE, B, S, Hq, Hkv, D, layout, comb, norm, dtype, None)
+    assert fv(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(layout=4) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(comb=2) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(norm=3) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(G=None) == _lib.GSA_ERR_INVALID_ARG           # a gate layout needs G
+    assert fv(layout=0) == _lib.GSA_ERR_INVALID_ARG         # no gate but G given
+    assert fv(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(D=96) == _lib.GSA_ERR_UNSUPPORTED
+    assert fv(Y=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert fv(LSE=FAKE + 2) == _lib.GSA_ERR_MISALIGNED
+    assert lib.gsa_last_error_message().decode().startswith("gsa_forward_variant")
+
+
+def test_value_gate_argument_checks(lib):
+    def vg(V=FAKE, G=FAKE, Vo=FAKE, B=1, S=8, Hkv=2, D=128, layout=1, dtype=1):
+        return lib.gsa_value_gate(V, G, Vo, B, S, Hkv, D, layout, dtype, None)
+    assert vg(V=None) == _lib.GSA_ERR_INVALID_ARG
+    assert vg(S=0) == _lib.GSA_ERR_INVALID_ARG
+    assert vg(layout=0) == _lib.GSA_ERR_INVALID_ARG
+    assert vg(layout=3) == _lib.GSA_ERR_INVALID_ARG
+    assert vg(D=32) == _lib.GSA_ERR_UNSUPPORTED
+    assert vg(dtype=9) == _lib.GSA_ERR_UNSUPPORTED
+    assert vg(G=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert lib.gsa_last_error_message().decode().startswith("gsa_value_gate")
 
 
 def test_project_qkvg_argument_checks(lib):

@@ -1,0 +1,117 @@
+"""The gate design-space variants on the GPU against the fp64 oracle: gate
+activations (gsa_gate_logits), layouts / combine / norm (gsa_forward_variant)
+and G2 value gating (gsa_value_gate + gsa_forward)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import variants as ov
+import gated_softmax_attention_amd as gsa
+from synth import CONFIGS, make_inputs
+from helpers import TOL, f64, report, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def draw_xw(M, dm, N, dtype, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    X = torch.randn(M, dm, generator=g, device=DEV).to(dtype)
+    W = (torch.randn(dm, N, generator=g, device=DEV) * (3.0 / math.sqrt(dm))).to(dtype)   # logits ~ N(0, 9)
+    return X, W
+
+
+@pytest.mark.parametrize("act", ["identity", "sigmoid", "ns_sigmoid", "silu"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("M,dm,N", [(37, 64, 5), (300, 2048, 256), (64, 4096, 32)])
+def test_gate_activations(M, dm, N, dtype, act):
+    X, W = draw_xw(M, dm, N, dtype, seed=M + N)
+    G = gsa.gate_logits(X, W, activation=act)
+    torch.cuda.synchronize()
+    want = ov.activation(oracle.gate_scores(f64(X), f64(W)), act)
+    # float32 accumulation of at most 4096 exact products: relative 1e-5 of the
+    # logits' scale; the activations are 1-Lipschitz up to |z| (SiLU)
+    tol = 1e-4 * max(1.0, float(np.abs(want).max()))
+    report(G.cpu().numpy(), want, tol, f"{act} {M}x{dm}x{N}")
+
+
+ACT_FOR = {("mul", "elementwise"): "sigmoid", ("mul", "headwise"): "ns_sigmoid", ("mul", "shared"): "sigmoid",
+           ("add", "elementwise"): "silu", ("add", "headwise"): "sigmoid", ("add", "shared"): "identity"}
+CASES = [(layout, combine, norm) for layout in ("elementwise", "headwise", "shared")
+         for combine in ("mul", "add") for norm in (None, "rms")] + [("none", "mul", "rms")]
+
+
+def gate_width(layout, Hq, D):
+    return {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 0}[layout]
+
+
+def run_variant(cfg, layout, combine, norm, seed, rows=None):
+    inp = make_inputs(cfg.with_(mode="none"), seed=seed, device=DEV)
+    N = gate_width(layout, cfg.Hq, cfg.D)
+    act = ACT_FOR.get((combine, layout), "sigmoid")
+    G = W = None
+    if N:
+        gx = torch.Generator(device=DEV).manual_seed(seed + 5)
+        W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
+        G = gsa.gate_logits(inp["X"], W, activation=act)
+    Y = gsa.forward_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm)
+    torch.cuda.synchronize()
+    want = ov.gated_sdpa_variant(f64(inp["X"]), None if W is None else f64(W), f64(inp["Q"]), f64(inp["K"]),
+                                 f64(inp["V"]), layout, act, combine, norm, rows=rows)
+    got = f64(Y) if rows is None else f64(Y[:, rows])
+    return got, want, act
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("layout,combine,norm", CASES)
+def test_forward_variant_small(layout, combine, norm, dtype):
+    for (B, S, Hq, Hkv, D) in [(2, 129, 8, 2, 128), (1, 200, 4, 4, 64)]:
+        cfg = CONFIGS["tiny_fp32"].with_(name="t", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, d_model=64)
+        got, want, act = run_variant(cfg, layout, combine, norm, seed=S + Hq)
+        # bf16: one rounding of an output of magnitude up to a few units
+        tol = TOL[dtype] * max(1.0, float(np.abs(want).max()) / 4)
+        report(got, want, tol, f"{dtype} {layout}/{combine}/{norm}/{act} B{B} S{S} {Hq}/{Hkv} D{D}")
+
+
+def test_default_variant_equals_forward_bitwise():
+    cfg = CONFIGS["tiny_fp32"].with_(name="t", B=2, S=300, Hq=8, Hkv=2, D=128, dtype="bf16", d_model=64,
+                                     mode="elementwise")
+    inp = make_inputs(cfg, seed=3, device=DEV)
+    G = gsa.gate_logits(inp["X"], inp["W"])
+    a = gsa.forward(inp["Q"], inp["K"], inp["V"], G, "elementwise")
+    b = gsa.forward_variant(inp["Q"], inp["K"], inp["V"], G, "elementwise", "mul", None)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["elementwise", "headwise"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_value_gating_g2(layout, dtype):
+    cfg = CONFIGS["tiny_fp32"].with_(name="t", B=2, S=257, Hq=8, Hkv=2, D=128, dtype=dtype, d_model=64,
+                                     mode="none")
+    inp = make_inputs(cfg, seed=11, device=DEV)
+    N = cfg.Hkv * cfg.D if layout == "elementwise" else cfg.Hkv
+    gx = torch.Generator(device=DEV).manual_seed(12)
+    Wv = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
+    Gv = gsa.gate_logits(inp["X"], Wv)
+    Vg = gsa.value_gate(inp["V"], Gv, layout)
+    Y = gsa.forward(inp["Q"], inp["K"], Vg, None, "none")
+    torch.cuda.synchronize()
+    want_v = ov.value_gate(f64(inp["X"]), f64(Wv), f64(inp["V"]), layout)
+    # the gated values are rounded once to the value dtype
+    report(f64(Vg), want_v, 2.0 ** -8 * float(np.abs(want_v).max()) if dtype == "bf16" else 1e-6,
+           f"V' {dtype} {layout}")
+    want = ov.value_gated_sdpa(f64(inp["X"]), f64(Wv), f64(inp["Q"]), f64(inp["K"]), f64(inp["V"]), layout)
+    report(f64(Y), want, TOL[dtype], f"G2 {dtype} {layout}")
+
+
+@pytest.mark.parametrize("layout,combine,norm", [("shared", "add", "rms"), ("headwise", "mul", "rms")])
+def test_forward_variant_dense_prefill_sampled(layout, combine, norm):
+    cfg = CONFIGS["dense_prefill"]
+    rows = sample_rows(cfg.S)
+    got, want, act = run_variant(cfg, layout, combine, norm, seed=0, rows=rows)
+    report(got, want, TOL["bf16"] * max(1.0, float(np.abs(want).max()) / 4),
+           f"dense_prefill {layout}/{combine}/{norm}/{act} sampled rows")

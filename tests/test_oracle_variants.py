@@ -136,3 +136,11 @@ def test_value_gate_g2():
                     z = math.fsum(t["X"][b, j, k] * t["W"][k, c * D + d] for k in range(dm))
                     Vg[b, j, c, d] = t["V"][b, j, c, d] * sig(z)
     assert np.max(np.abs(got - oracle.sdpa(t["Q"], t["K"], Vg))) <= 1e-14
+
+
+def test_rows_subset_equals_full():
+    t = draw(np.random.default_rng(9), 2, 30, 4, 2, 4, 6, 4)
+    full = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "silu", "add", "rms")
+    rows = [0, 7, 29]
+    part = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "silu", "add", "rms", rows=rows)
+    assert np.array_equal(part, full[:, rows])
