@@ -113,8 +113,10 @@ gsa_status check_dtype(const char* fn, int dtype) {
   return GSA_OK;
 }
 
+// S is the key/value length; Sq the query rows per batch (S for prefill, 1 for decode).
 gsa_status check_attn_shape(const char* fn, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
-                            int mode, const float* G) {
+                            int mode, const float* G, int64_t Sq = -1) {
+  if (Sq < 0) Sq = S;
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0)
     return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%lld S=%lld Hq=%lld Hkv=%lld D=%lld)",
                 fn, (long long)B, (long long)S, (long long)Hq, (long long)Hkv, (long long)D);
@@ -130,7 +132,8 @@ gsa_status check_attn_shape(const char* fn, int64_t B, int64_t S, int64_t Hq, in
   if (B * S > kIntMax || Hq > 4096 || Hkv > 4096 || S > kIntMax)
     return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
   // the kernels address one batch's Q / K / V rows with 32-bit byte offsets
-  if (S * Hq * D * 4 > kIntMax)
+  // (bounded here at the float32 size)
+  if (Sq * Hq * D * 4 > kIntMax || S * Hkv * D * 4 > kIntMax)
     return fail(GSA_ERR_UNSUPPORTED, "%s: one batch of Q or K/V exceeds 2 GiB", fn);
   return GSA_OK;
 }
@@ -229,7 +232,7 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
                       int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!Q || !Kc || !Vc || !Y) return fail(GSA_ERR_INVALID_ARG, "gsa_decode: null pointer");
-  if (gsa_status st = check_attn_shape("gsa_decode", B, L, Hq, Hkv, D, mode, G)) return st;
+  if (gsa_status st = check_attn_shape("gsa_decode", B, L, Hq, Hkv, D, mode, G, 1)) return st;
   if (gsa_status st = check_dtype("gsa_decode", dtype)) return st;
   if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "gsa_decode: num_splits must be >= 0");
   if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "gsa_decode: B*L exceeds the supported range");

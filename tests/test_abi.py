@@ -108,6 +108,17 @@ def test_decode_argument_checks(lib):
     assert dec(ws=MIS) == _lib.GSA_ERR_MISALIGNED
 
 
+def test_size_limits(lib):
+    # one batch of Q (prefill) above 2 GiB at the float32 size
+    assert fwd(lib, S=1 << 20, Hq=8, Hkv=8, D=128) == _lib.GSA_ERR_UNSUPPORTED
+    # decode: the limit is the cache's own size (L x Hkv x D), not L x Hq
+    dec = lambda L, Hkv: lib.gsa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, L, 32, Hkv, 128, 1, 1, 0, FAKE,
+                                        1 << 40, None)
+    assert dec(1 << 21, 8) == _lib.GSA_ERR_UNSUPPORTED               # 2M x 8 x 128 x 4 B > 2 GiB
+    if not have_gpu():
+        assert dec(1 << 18, 8) == _lib.GSA_ERR_NO_DEVICE             # 256k x 32 query heads passes
+
+
 def test_decode_split_arithmetic(lib):
     # requested counts are honoured up to the chunk rounding; every split is non-empty
     for L, ns in [(16384, 16), (1, 0), (1, 4), (63, 0), (1025, 3), (100, 7), (16384, 0)]:

@@ -94,3 +94,11 @@ def test_full_size_decode_config():
     bs = [0, 17, 63]
     want = oracle_decode(inp, cfg.mode, batches=bs)
     report(f64(Y[bs]), want, TOL["bf16"], f"decode full size, batches {bs}")
+
+
+def test_decode_long_cache():
+    """A 262144-long cache (one batch, 32/8 heads, elementwise gate)."""
+    cfg = dec_cfg(1, 262144, 32, 8, 128, "elementwise", "bf16")
+    inp = make_inputs(cfg, seed=9, device=DEV)
+    Y, _ = run(inp, "elementwise")
+    report(f64(Y), oracle_decode(inp, "elementwise"), TOL["bf16"], "decode L=262144")

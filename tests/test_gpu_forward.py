@@ -179,3 +179,31 @@ def test_full_size_config_sampled_rows(name):
     g0 = g0.view(cfg.B, cfg.Hq, cfg.D) if cfg.mode == "elementwise" else g0.view(cfg.B, cfg.Hq, 1)
     assert torch.equal(Y[:, 0].view(torch.int16), (v0 * g0).to(torch.bfloat16).view(torch.int16))
     assert not torch.isnan(Y.float()).any()
+
+
+# --------------------------------------------------------------- extremes
+def test_long_sequence_near_the_size_limit_sampled():
+    """S = 131072 (one batch, 4 query heads on 1 key/value head, headwise gate):
+    the last query rows see 131072 keys; sampled rows against the oracle."""
+    cfg = CONFIGS["long_prefill"].with_(name="s128k", B=1, S=131072, d_model=64, Hq=4, Hkv=1,
+                                        mode="headwise", sink_scale=1.0)
+    inp = make_inputs(cfg, seed=5, device=DEV)
+    Y, G = run(inp, cfg.mode, guard=False)
+    rows = [0, 1, 4095, 65536, 131070, 131071]
+    idx = torch.tensor(rows, device=DEV)
+    want = oracle_rows(f64(inp["X"][:, idx]), f64(inp["W"]), f64(inp["Q"][:, idx]),
+                       f64(inp["K"]), f64(inp["V"]), cfg.mode, rows)
+    report(f64(Y[:, idx]), want, TOL["bf16"], "S=131072 sampled rows")
+    assert not torch.isnan(Y.float()).any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_scores(dtype):
+    """Q and K scaled by 8: scores reach several hundred, rows are nearly one-hot
+    and the running maximum moves by large steps."""
+    cfg = small_cfg(2, 333, 8, 2, 128, "elementwise", dtype)
+    inp = make_inputs(cfg, seed=41, device=DEV)
+    for k in ("Q", "K"):
+        inp[k] = (inp[k].float() * 8).to(inp[k].dtype)   # exact: a power of two
+    Y, _ = run(inp, "elementwise")
+    report(f64(Y), full_oracle(inp, "elementwise"), TOL[dtype], f"{dtype} scores x64")
