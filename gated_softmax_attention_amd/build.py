@@ -1,6 +1,6 @@
 """Build libgsa.so (all HIP kernels + the C ABI) in-tree with hipcc for gfx950.
 
-Usage:  python -m gated_softmax_attention_amd.build   (or __graft_entry__.build())
+Usage:  python -m gated_softmax_attention_amd.build
 """
 import os
 import shutil
