@@ -204,8 +204,10 @@ __device__ __forceinline__ void pack_b(const f32x16 (&s)[2], bf16x8 (&pb)[2][2])
 // 256 threads: 128 query rows of one head (4 waves x 32); key tiles of 64.
 //   Sᵀ = K·Qᵀ, dPᵀ = V·dYᵀ  (A = K / V rows from LDS, B = Q / dY fragments)
 //   dQᵀ += Kᵀ·dSᵀ          (A = K through transposed reads, B = dS in bf16)
+// Two workgroups per CU (≤ 256 registers, 68 KB of LDS each): the second
+// workgroup's waves hide the first's LDS and barrier waits.
 template <int D>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, 2)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                    const bf16* __restrict__ dY, const float* __restrict__ Stat,
                    bf16* __restrict__ dQ, int B, int S, int Hq, int Hkv, int n_qtiles, int Sp,
@@ -350,8 +352,11 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 // The query heads of a group may be cut into `nsplit` slices (one workgroup
 // each) so small-Hkv shapes still fill the chip; slices then write float32
 // partial sums [nsplit][B][S][Hkv][D] that bwd_sum_slices adds in order.
+// One workgroup per CU at D = 128: K, V fragments, the dK/dV accumulators and
+// S/dP need ≈ 360 registers (forcing 256 spills 47 and runs 7% slower); two at
+// D = 64.
 template <int D, bool PARTIAL>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1)
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      const bf16* __restrict__ dY, const float* __restrict__ Stat,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKp,
