@@ -190,11 +190,24 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
   const int l32 = lane & 31, hl = lane >> 5;
 
   // tile index: XCD x = bid % 8 takes the x-th contiguous eighth of the
-  // row-major tile list when the tile count divides evenly
+  // row-major tile list when the tile count divides evenly.  When that eighth
+  // spans more than 8 column tiles (the fused projection), its tiles go in
+  // rounds of 4 row tiles x 8 column tiles (32 workgroups, one per CU of the
+  // XCD), so a round reads 4 X row blocks and 8 W column blocks and each W
+  // column block passes through the XCD's L2 once.
   const int T = tiles_m * tiles_n;
   const int bid = blockIdx.x;
-  const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
-  const int tm = t / tiles_n, tn = t % tiles_n;
+  int tm, tn;
+  if (T % 8 == 0 && tiles_m % 32 == 0 && tiles_n % 8 == 0 && tiles_n > 8) {
+    const int tm_per = tiles_m / 8, x = bid % 8, j = bid / 8;
+    const int in = j % 8, im = (j / 8) % 4, blk = j / 32, nbn = tiles_n / 8;
+    tm = x * tm_per + (blk / nbn) * 4 + im;
+    tn = (blk % nbn) * 8 + in;
+  } else {
+    const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    tm = t / tiles_n;
+    tn = t % tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   const auto xr = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
