@@ -267,3 +267,33 @@ def test_python_binding_refuses_cpu_tensors():
     w = torch.zeros(64, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         gsa.gate_logits(x, w, G=torch.zeros(4, 8))
+
+
+def test_error_messages_are_per_thread(lib):
+    """Calls are thread-safe and the last-error message is per thread: threads
+    making different invalid calls each read back their own message."""
+    import threading
+    results = {}
+
+    def work(i):
+        msgs = []
+        for _ in range(200):
+            if i % 3 == 0:
+                st = fwd(lib, D=96)                                   # unsupported head dim
+                want = "gsa_forward"
+            elif i % 3 == 1:
+                st = lib.gsa_gate_logits(FAKE, FAKE, FAKE, 4, 60, 8, 1, 1, None)   # d_model % 8
+                want = "gsa_gate_logits"
+            else:
+                st = bwd(lib, dtype=0)                                # fp32 backward
+                want = "gsa_backward"
+            msgs.append((st, lib.gsa_last_error_message().decode().startswith(want)))
+        results[i] = msgs
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(9)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, msgs in results.items():
+        assert all(st == _lib.GSA_ERR_UNSUPPORTED and ok for st, ok in msgs), i
