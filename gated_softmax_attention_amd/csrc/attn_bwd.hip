@@ -128,11 +128,14 @@ struct Tile {
 
 // Direct loads of `rows` rows of a [*, stride] bf16 tensor into a padded tile:
 // 4 waves, wave instruction i covers slots 64*i .. 64*i+63.  Rows at or past
-// `row_end` and the pad slot read zeros.
+// `row_end` and the pad slot read zeros.  Every instruction writes all 64
+// slots, so the LDS buffer must hold kBytes (whole instructions), which exceeds
+// ROWS row strides when ROWS * SL is not a multiple of 64.
 template <int D, int ROWS>
 struct TileLoader {
   static constexpr int SL = Tile<D>::SL;
   static constexpr int NI = (ROWS * SL + 255) / 256;   // instructions per wave
+  static constexpr int kBytes = (ROWS * SL + 63) / 64 * 1024;
   uint32_t off[NI];
   uint32_t ins_base[NI];
   __device__ void init(int wave, int lane, uint32_t row_bytes) {
@@ -214,6 +217,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    float scale) {
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
+  static_assert(TileLoader<D, KT>::kBytes == KT * RSB, "key tile is not a whole number of loads");
   __shared__ __align__(16) char Ks[2][KT * RSB];
   __shared__ __align__(16) char Vs[2][KT * RSB];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -352,9 +356,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 // The query heads of a group may be cut into `nsplit` slices (one workgroup
 // each) so small-Hkv shapes still fill the chip; slices then write float32
 // partial sums [nsplit][B][S][Hkv][D] that bwd_sum_slices adds in order.
-// One workgroup per CU at D = 128: K, V fragments, the dK/dV accumulators and
-// S/dP need ≈ 360 registers (forcing 256 spills 47 and runs 7% slower); two at
-// D = 64.
+// Launched at D = 64 (two workgroups per CU).  At D = 128 this arrangement
+// needs ≈ 360 registers (one workgroup per CU); bwd_dkdv_vlds_kernel replaces it
+// there.
 template <int D, bool PARTIAL>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1)
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -364,6 +368,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
                      float scale) {
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
+  static_assert(TileLoader<D, QW>::kBytes == QW * RSB, "query tile is not a whole number of loads");
   __shared__ __align__(16) char Qs[2][QW * RSB];
   __shared__ __align__(16) char Ys[2][QW * RSB];
   __shared__ __align__(16) float Ss[2][256];   // per stage: base-2 LSE of 64 rows, D of 64 rows, pad
@@ -535,6 +540,198 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     }
 }
 
+// ---------------------------------------------------------------- dK, dV at D = 128
+// The same products as bwd_dkdv_kernel, arranged to fit two workgroups per CU
+// (≤ 256 registers, 72 KB of LDS each) so one workgroup's waves cover the
+// other's LDS and barrier waits:
+//   * V of the workgroup's 128 keys is staged once in LDS and read back as the
+//     B operand of dP (a 16-byte row read per k step) instead of living in
+//     registers;
+//   * query tiles are 32 rows, halving the S and dP accumulators.
+// K fragments and the dK/dV accumulators stay in registers.
+template <int D, bool PARTIAL>
+__global__ __launch_bounds__(256, 2)
+void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                          const bf16* __restrict__ dY, const float* __restrict__ Stat,
+                          bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKp,
+                          float* __restrict__ dVp, int B, int S, int Hq, int Hkv, int Sp, int nsplit,
+                          float scale) {
+  using namespace bwd;
+  constexpr int RSB = Tile<D>::RSB;
+  constexpr int QR = 32;   // query rows per staged tile
+  constexpr int QB = TileLoader<D, QR>::kBytes;   // 9 KB: 32 padded rows rounded up to whole loads
+  __shared__ __align__(16) char Vt[TileLoader<D, KW>::kBytes];
+  __shared__ __align__(16) char Qs[2][QB];
+  __shared__ __align__(16) char Ys[2][QB];
+  __shared__ __align__(16) float Ss[2][256];   // per stage: base-2 LSE of 32 rows, D of 32 rows, pad
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int bid = blockIdx.x;
+  const int hb = Hkv * B * nsplit;
+  const int kt_i = bid / hb;                       // early key tiles see the most queries: first
+  const int rest = bid % hb;
+  const int slice = rest % nsplit, pair = rest / nsplit;
+  const int kvh = pair % Hkv, b = pair / Hkv;
+  const int G = Hq / Hkv, Gs = G / nsplit;
+  const int k0 = kt_i * KW, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  const int64_t q_row = (int64_t)Hq * D, kv_row = (int64_t)Hkv * D;
+  const float scale_log2 = scale * kLog2e;
+
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)S * kv_row - (int64_t)kvh * D) * 2);
+  const uint32_t kv_row_b = (uint32_t)(kv_row * 2);
+  const auto vr = make_rsrc(V + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+  {
+    TileLoader<D, KW> vld;
+    vld.init(wave, lane, kv_row_b);
+    vld.load(vr, kv_row_b, k0, S, __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0])), wave);
+  }
+  // K fragments (B operands) of this lane's key
+  bf16x8 kf[D / 16];
+  {
+    const auto kr = make_rsrc(K + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
+    const uint32_t o = (uint32_t)(((int64_t)my_k * kv_row + 8 * hl) * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, buffer_load16(kr, o + 32 * kk, 0));
+    // settled here so the loop's waits do not re-wait for them
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]));
+  }
+  const uint32_t row_b = (uint32_t)(q_row * 2);
+  TileLoader<D, QR> ld;
+  ld.init(wave, lane, row_b);
+  uint32_t qs_lds[2], ys_lds[2], st_lds[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    qs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Qs[i][0]));
+    ys_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ys[i][0]));
+    st_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ss[i][0]));
+  }
+  // statistics loads (wave 0): lanes 0..7 take 4 LSE rows each, lanes 8..15 4 D rows
+  const auto srs = make_rsrc(Stat, (uint32_t)((int64_t)2 * B * Hq * Sp * 4));
+  const uint32_t st_lane = lane < 8 ? 16u * lane : (uint32_t)((int64_t)B * Hq * Sp * 4) + 16u * (lane - 8);
+  uint32_t trb[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+
+  // query tiles that see keys [k0, k0 + KW): rows >= k0
+  const int qt_first = k0 / QR;
+  const int n_qt = ceil_div(S, QR) - qt_first;
+  const int n_steps = Gs * max(n_qt, 0);
+  const int head0 = kvh * G + slice * Gs;
+  auto tile_of = [&](int step, int& head, int& qs0) {
+    head = head0 + step / n_qt;
+    qs0 = (qt_first + step % n_qt) * QR;
+  };
+  auto issue = [&](int step, int buf) {
+    int head, qs0;
+    tile_of(step, head, qs0);
+    const uint32_t bytes = (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2);
+    const auto qr = make_rsrc(Q + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
+    const auto yr = make_rsrc(dY + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
+    ld.load(qr, row_b, qs0, S, qs_lds[buf], wave);
+    ld.load(yr, row_b, qs0, S, ys_lds[buf], wave);
+    if (wave == 0)
+      dma16_lds(srs, lane < 16 ? st_lane + (uint32_t)(((int64_t)b * Hq + head) * Sp + qs0) * 4u : kOOB,
+                st_lds[buf]);
+  };
+  const GSA_LDS_B char* vt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Vt[0];
+  if (n_steps > 0) issue(0, 0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    int head, qs0;
+    tile_of(step, head, qs0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (step + 1 < n_steps) issue(step + 1, buf ^ 1);
+    // a wave whose keys all come after the tile's last query gets P = dS = 0
+    if (kw0 > qs0 + QR - 1) continue;
+    const GSA_LDS_B char* qt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Qs[buf][0];
+    const GSA_LDS_B char* yt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ys[buf][0];
+    const GSA_LDS_B float* st = (const GSA_LDS_B float*)(GSA_LDS_B void*)&Ss[buf][0];
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma32x32x16(row_read<D>(qt, l32, kk, hl), kf[kk], s);
+      dp = mfma32x32x16(row_read<D>(yt, l32, kk, hl), row_read<D>(vt, wave * 32 + l32, kk, hl), dp);
+    }
+    // element r: query qs0 + 8*(r/4) + 4*hl + r%4, key my_k.  Masked where the
+    // wave's keys pass the tile's first query or the tile runs past S (rows
+    // past S hold zero statistics and must not count).
+    if ((qs0 < kw0 + 31) || (qs0 + QR > S)) {
+      const int lo = my_k - qs0 - 4 * hl, hi = S - 1 - qs0 - 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off < lo || off > hi) s[r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row4 = 8 * i + 4 * hl;
+      const f32x4 l4 = *(const GSA_LDS_B f32x4*)(st + row4);
+      const f32x4 d4 = *(const GSA_LDS_B f32x4*)(st + QR + row4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
+        const float p = fast_exp2(fmaf(s[r], scale_log2, -l4[j]));
+        dp[r] = p * (dp[r] - d4[j]);   // dS
+        s[r] = p;
+      }
+    }
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[t][e] = (bf16)s[8 * t + e];
+        db[t][e] = (bf16)dp[8 * t + e];
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int ro = 16 * t * RSB;
+        dv[dt] = mfma32x32x16(tr_read(yt + trb[dt] + ro, RSB), pb[t], dv[dt]);
+        dk[dt] = mfma32x32x16(tr_read(qt + trb[dt] + ro, RSB), db[t], dk[dt]);
+      }
+  }
+
+  if (my_k >= S) return;
+  const int64_t orow = ((int64_t)b * S + my_k) * kv_row + (int64_t)kvh * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = dt * 32 + 8 * i + 4 * hl;
+      if constexpr (PARTIAL) {
+        const int64_t o = (int64_t)slice * B * S * kv_row + orow + d0;
+        *(f32x4*)(dKp + o) = f32x4{dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale,
+                                   dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale};
+        *(f32x4*)(dVp + o) = f32x4{dv[dt][4 * i], dv[dt][4 * i + 1], dv[dt][4 * i + 2], dv[dt][4 * i + 3]};
+      } else {
+        *(u32x2*)(dK + orow + d0) = u32x2{pack_bf16x2(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale),
+                                          pack_bf16x2(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale)};
+        *(u32x2*)(dV + orow + d0) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
+                                          pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+      }
+    }
+}
+
 // dK, dV (bf16) = Σ over slices of the float32 partial sums, in slice order;
 // 4 elements per thread (n4 = element count / 4).
 __global__ __launch_bounds__(256)
@@ -592,17 +789,25 @@ static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, cons
   const int nk = ceil_div(S, bwd::KW);
   const int ns = bwd_kv_slices(B, S, Hq, Hkv);
   const unsigned grid = (unsigned)((int64_t)nk * Hkv * B * ns);
+  constexpr bool vlds = D == 128;
+  auto dkdv = [&](auto partial, bf16* dk, bf16* dv, float* dkp, float* dvp) {
+    constexpr bool P = decltype(partial)::value;
+    if constexpr (vlds)
+      hipLaunchKernelGGL((bwd_dkdv_vlds_kernel<D, P>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
+                         (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
+                         Hq, Hkv, Sp, ns, scale);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, P>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
+                         (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
+                         Hq, Hkv, Sp, ns, scale);
+  };
   if (ns == 1) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, (bf16*)dK, (bf16*)dV,
-                       nullptr, nullptr, B, S, Hq, Hkv, Sp, 1, scale);
+    dkdv(std::false_type{}, (bf16*)dK, (bf16*)dV, nullptr, nullptr);
   } else {
     const int64_t n = (int64_t)B * S * Hkv * D;
     float* dKp = part;
     float* dVp = part + ns * n;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, nullptr, nullptr, dKp,
-                       dVp, B, S, Hq, Hkv, Sp, ns, scale);
+    dkdv(std::true_type{}, nullptr, nullptr, dKp, dVp);
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div<int64_t>(n / 4, 256), 4096);
     hipLaunchKernelGGL(bwd_sum_slices_kernel, dim3(blocks), dim3(256), 0, st, (const f32x4*)dKp,
                        (const f32x4*)dVp, (u32x2*)dK, (u32x2*)dV, n / 4, ns);
