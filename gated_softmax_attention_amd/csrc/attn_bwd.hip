@@ -15,13 +15,14 @@
 // Two kernels recompute S and dP instead of one with atomics, so the result is
 // deterministic.
 //
-// Layout in LDS: every staged tile is [row][d] with a 272-byte row stride (one
-// 16-byte pad slot per row), filled by 16-byte direct loads.  Row reads (MFMA
-// operands with 8 consecutive d) are conflict-free; transposed reads
-// (ds_read_b64_tr_b16, operands with 8 consecutive rows) see 2-way conflicts.
-// The transposed-read addressing permutes rows inside each 16-row block so a
-// lane's 8 rows match the accumulator layout of S, exactly as the forward's PV
-// product does with its probabilities.
+// Layout in LDS: every staged tile is [row][d], filled by 16-byte direct loads
+// and read both by rows (MFMA operands with 8 consecutive d) and transposed
+// (ds_read_b64_tr_b16, operands with 8 consecutive rows).  At D = 128 the rows
+// are 256 bytes with an XOR swizzle of their 16-byte chunks that keeps both
+// kinds of read free of bank conflicts (Tile below); at D = 64 they are
+// padded to 144 bytes.  The transposed-read addressing permutes rows inside
+// each 16-row block so a lane's 8 rows match the accumulator layout of S,
+// exactly as the forward's PV product does with its probabilities.
 #include <type_traits>
 
 #include "common.h"
@@ -118,19 +119,37 @@ void bwd_prep_kernel(const bf16* __restrict__ dYg, const bf16* __restrict__ Yg,
 }
 
 // ---------------------------------------------------------------- shared pieces
-// Staged tile: ROWS rows of D bf16, 272-byte (D=128) / 144-byte (D=64) stride.
+// Staged tile: rows of D bf16, each read two ways: 16-byte row reads (8
+// consecutive dims of one row: the A operand of S-type products) and
+// transposed reads (4 dims of 4 consecutive rows per lane: the A operand of
+// products whose k runs over rows).  Both must avoid LDS bank conflicts.
+//   D = 64: 144-byte rows, 8 chunks of 16 bytes plus one pad slot.
+//   D = 128: 256-byte rows with no pad; chunk c of row r sits in slot
+//            c ^ tile_swz(r), tile_swz(r) = 4·(r & 3) + ((r >> 2) & 3).
+// tile_swz is a bijection on any 16 consecutive rows, so the 16 rows of a row
+// read land in 16 different slots.  A transposed read touches rows R..R+3
+// (R a multiple of 4) and chunks 4m..4m+3 over 32 lanes; tile_swz(R + j)
+// differs in bits 2..3 for the four j, so those 16 (row, chunk) pairs also
+// land in 16 different slots, one per group of four banks.  (A padded 272-byte
+// row instead puts neighbouring rows of a transposed read on overlapping banks.)
+__host__ __device__ constexpr int tile_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
 template <int D>
 struct Tile {
-  static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int SL = CH + 1;         // slots per row (one pad slot)
-  static constexpr int RSB = SL * 16;       // row stride in bytes
+  static constexpr bool SWZ = D == 128;
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int SL = SWZ ? CH : CH + 1;     // slots per row
+  static constexpr int RSB = SL * 16;              // row stride in bytes
+  // byte offset, within its row, of chunk c of row `row`
+  static __device__ __forceinline__ int chunk_off(int row, int c) { return (SWZ ? c ^ tile_swz(row) : c) * 16; }
 };
 
-// Direct loads of `rows` rows of a [*, stride] bf16 tensor into a padded tile:
-// 4 waves, wave instruction i covers slots 64*i .. 64*i+63.  Rows at or past
-// `row_end` and the pad slot read zeros.  Every instruction writes all 64
-// slots, so the LDS buffer must hold kBytes (whole instructions), which exceeds
-// ROWS row strides when ROWS * SL is not a multiple of 64.
+// Direct loads of `rows` rows of a [*, stride] bf16 tensor into a tile: 4
+// waves, wave instruction i covers slots 64*i .. 64*i+63 (slot s = row·SL +
+// physical chunk).  Rows at or past `row_end` and the pad slot read zeros.
+// Every instruction writes all 64 slots, so the LDS buffer must hold kBytes
+// (whole instructions), which exceeds ROWS row strides when ROWS * SL is not a
+// multiple of 64.
 template <int D, int ROWS>
 struct TileLoader {
   static constexpr int SL = Tile<D>::SL;
@@ -144,7 +163,9 @@ struct TileLoader {
       const int ins = wave + 4 * j;
       const int sl = ins * 64 + lane;
       const int row = sl / SL, ch = sl % SL;
-      off[j] = (ch < Tile<D>::CH && row < ROWS) ? (uint32_t)row * row_bytes + ch * 16 : kOOBv();
+      // the logical chunk stored in physical slot ch (the swizzle is its own inverse)
+      const int c = Tile<D>::SWZ ? ch ^ tile_swz(row) : ch;
+      off[j] = (ch < Tile<D>::CH && row < ROWS) ? (uint32_t)row * row_bytes + c * 16 : kOOBv();
       ins_base[j] = (uint32_t)ins * 64 * 16;
     }
   }
@@ -165,35 +186,43 @@ struct TileLoader {
   }
 };
 
-// Transposed-read address of a lane inside a padded tile for the A operand of
-// an MFMA whose k index runs over tile rows: rows 16t + 8a + 4*hl + 0..3 of a
+// Transposed-read addresses of a lane inside a tile for the A operand of an
+// MFMA whose k index runs over tile rows: rows 16t + 8a + 4*hl + 0..3 of a
 // 16-row block land in k slots 4a..4a+3 of lane half hl (the accumulator layout
-// of S), dims dt*32 + (lane within 32).
+// of S), dims dt*32 + (lane within 32).  The lane's first read names row
+// r = 4*(g/2) + i/4 (g = lane/16, i = lane%16), the second row r + 8; both
+// name dims dt*32 + 16*(g%2) + 4*(i%4) .. +3.  Adding a multiple of 16 rows
+// keeps the swizzle, so one pair of offsets serves every 16-row block.
+struct TrAddr {
+  uint32_t lo, hi;
+};
 template <int D>
-__device__ __forceinline__ uint32_t tr_base(int lane, int dt) {
+__device__ __forceinline__ TrAddr tr_addr(int lane, int dt) {
   const int vg = lane >> 4, vi = lane & 15;
   const int r = 4 * (vg >> 1) + (vi >> 2);
-  const int dc = 16 * (vg & 1) + 4 * (vi & 3);
-  return (uint32_t)(r * Tile<D>::RSB + (dt * 32 + dc) * 2);
+  const int dc = dt * 32 + 16 * (vg & 1) + 4 * (vi & 3);   // first of the lane's 4 dims
+  const int c = dc / 8, in = (dc % 8) * 2;                  // its chunk and byte within the chunk
+  return TrAddr{(uint32_t)(r * Tile<D>::RSB + Tile<D>::chunk_off(r, c) + in),
+                (uint32_t)((r + 8) * Tile<D>::RSB + Tile<D>::chunk_off(r + 8, c) + in)};
 }
 
-__device__ __forceinline__ bf16x8 tr_read(const GSA_LDS_B char* p, int rsb) {
-  const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)p);
-  const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)(p + 8 * rsb));
-  bf16x8 a;
-  a.lo = __builtin_bit_cast(bf16x4, lo);
-  a.hi = __builtin_bit_cast(bf16x4, hi);
-  return a;
+__device__ __forceinline__ bf16x8 tr_read(const GSA_LDS_B char* blk, const TrAddr& a) {
+  const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)(blk + a.lo));
+  const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_B i16x4*)(blk + a.hi));
+  bf16x8 r;
+  r.lo = __builtin_bit_cast(bf16x4, lo);
+  r.hi = __builtin_bit_cast(bf16x4, hi);
+  return r;
 }
 
 // Row read: row `row`, dims 16*kk + 8*hl .. +7 (the A operand of S-type products).
 template <int D>
 __device__ __forceinline__ bf16x8 row_read(const GSA_LDS_B char* tile, int row, int kk, int hl) {
-  return *(const GSA_LDS_B bf16x8*)(tile + row * Tile<D>::RSB + (2 * kk + hl) * 16);
+  return *(const GSA_LDS_B bf16x8*)(tile + row * Tile<D>::RSB + Tile<D>::chunk_off(row, 2 * kk + hl));
 }
 
 // Accumulator pair (2 x 32 rows of a 64-row block, 16 regs each) -> bf16 B
-// operands, k order matching tr_base's row permutation.
+// operands, k order matching tr_addr's row permutation.
 __device__ __forceinline__ void pack_b(const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -267,9 +296,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     ks_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[i][0]));
     vs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[i][0]));
   }
-  uint32_t trb[D / 32];
+  TrAddr trb[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_addr<D>(lane, dt);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -332,7 +361,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-          acc[dt] = mfma32x32x16(tr_read(kt + trb[dt] + (sub * 32 + 16 * t) * RSB, RSB), ds[sub][t], acc[dt]);
+          acc[dt] = mfma32x32x16(tr_read(kt + (sub * 32 + 16 * t) * RSB, trb[dt]), ds[sub][t], acc[dt]);
   }
 
   if (my_q >= S) return;
@@ -416,9 +445,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // statistics loads (wave 0): lanes 0..15 take 4 LSE rows each, lanes 16..31 4 D rows
   const auto srs = make_rsrc(Stat, (uint32_t)((int64_t)2 * B * Hq * Sp * 4));
   const uint32_t st_lane = lane < 16 ? 16u * lane : (uint32_t)((int64_t)B * Hq * Sp * 4) + 16u * (lane - 16);
-  uint32_t trb[D / 32];
+  TrAddr trb[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_addr<D>(lane, dt);
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -514,8 +543,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const int ro = (sub * 32 + 16 * t) * RSB;
-          dv[dt] = mfma32x32x16(tr_read(yt + trb[dt] + ro, RSB), pb[sub][t], dv[dt]);
-          dk[dt] = mfma32x32x16(tr_read(qt + trb[dt] + ro, RSB), db[sub][t], dk[dt]);
+          dv[dt] = mfma32x32x16(tr_read(yt + ro, trb[dt]), pb[sub][t], dv[dt]);
+          dk[dt] = mfma32x32x16(tr_read(qt + ro, trb[dt]), db[sub][t], dk[dt]);
         }
   }
 
@@ -559,7 +588,7 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
   constexpr int QR = 32;   // query rows per staged tile
-  constexpr int QB = TileLoader<D, QR>::kBytes;   // 9 KB: 32 padded rows rounded up to whole loads
+  constexpr int QB = TileLoader<D, QR>::kBytes;   // 32 rows, rounded up to whole loads
   __shared__ __align__(16) char Vt[TileLoader<D, KW>::kBytes];
   __shared__ __align__(16) char Qs[2][QB];
   __shared__ __align__(16) char Ys[2][QB];
@@ -610,9 +639,9 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // statistics loads (wave 0): lanes 0..7 take 4 LSE rows each, lanes 8..15 4 D rows
   const auto srs = make_rsrc(Stat, (uint32_t)((int64_t)2 * B * Hq * Sp * 4));
   const uint32_t st_lane = lane < 8 ? 16u * lane : (uint32_t)((int64_t)B * Hq * Sp * 4) + 16u * (lane - 8);
-  uint32_t trb[D / 32];
+  TrAddr trb[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_base<D>(lane, dt);
+  for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_addr<D>(lane, dt);
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -706,8 +735,8 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int ro = 16 * t * RSB;
-        dv[dt] = mfma32x32x16(tr_read(yt + trb[dt] + ro, RSB), pb[t], dv[dt]);
-        dk[dt] = mfma32x32x16(tr_read(qt + trb[dt] + ro, RSB), db[t], dk[dt]);
+        dv[dt] = mfma32x32x16(tr_read(yt + ro, trb[dt]), pb[t], dv[dt]);
+        dk[dt] = mfma32x32x16(tr_read(qt + ro, trb[dt]), db[t], dk[dt]);
       }
   }
 
