@@ -446,6 +446,26 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
         ss += __shfl_xor(ss, 32);   // lane ^ 32 holds the same row (same my_q: both take this path)
         rn = 1.0f / sqrtf(ss / (float)D + kRmsEps);
       }
+      // the row's gate values, all loaded before the first store of Y (see below)
+      f32x4 gv[D / 32][4];
+      if (ep.layout != kGateNone) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = dt * 32 + 8 * i + 4 * hl;
+            if (ep.layout == kGateHead) {
+              const float g = Gate[tok * Hq + head];
+              gv[dt][i] = f32x4{g, g, g, g};
+            } else {
+              gv[dt][i] = *(const f32x4*)(Gate + (ep.layout == kGateElem ? (tok * Hq + head) * D : tok * D) + d0);
+            }
+          }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(gv[dt][i]));
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -455,8 +475,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             y[j] = o[qb][dt][4 * i + j] * inv * rn;
-            if (ep.layout != kGateNone)
-              y[j] = variant_combine(y[j], variant_gate(Gate, ep, tok, Hq, D, head, d0 + j), ep);
+            if (ep.layout != kGateNone) y[j] = variant_combine(y[j], gv[dt][i][j], ep);
           }
           *(u32x2*)(yrow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         }
@@ -464,6 +483,21 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     float gh = 1.0f;
     if constexpr (MODE == kGateHead) gh = Gate[tok * Hq + head];
+    // elementwise gate: all of the row's gate loads are issued before the first
+    // store of Y.  The memory counter the waits use also counts stores, so a
+    // gate load issued after a store would wait for that store to complete.
+    f32x4 gv[D / 32][4];
+    if constexpr (MODE == kGateElem) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gv[dt][i] = *(const f32x4*)(Gate + tok * q_row + (int64_t)head * D + dt * 32 + 8 * i + 4 * hl);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(gv[dt][i]));
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -473,9 +507,8 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
         for (int j = 0; j < 4; ++j) y[j] = o[qb][dt][4 * i + j] * inv;
         if constexpr (MODE == kGateElem) {
-          const f32x4 g = *(const f32x4*)(Gate + tok * q_row + (int64_t)head * D + d0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] *= g[j];
+          for (int j = 0; j < 4; ++j) y[j] *= gv[dt][i][j];
         } else if constexpr (MODE == kGateHead) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] *= gh;
