@@ -167,17 +167,22 @@ def test_backward_is_deterministic():
 
 
 # --------------------------------------------------------------- full workload size, sampled
-def test_backward_dense_prefill_full_size_sampled():
-    """gsa_backward on the whole dense-prefill workload (B 2, S 4096, 16/16 heads,
-    D 128, d_model 2048, elementwise gate), in the configuration the bench
-    times; the oracle computes two key/value heads' dQ, dK, dV, their dW_θ
-    columns (every token) and a sample of dX rows exactly."""
+@pytest.mark.parametrize("name", ["dense_prefill", "gqa_prefill"])
+def test_backward_full_size_sampled(name):
+    """gsa_backward on a whole workload, in the launch configuration the bench
+    uses for dense_prefill (B 2, S 4096, 16/16 heads, D 128, d_model 2048,
+    elementwise gate: one workgroup per key tile and head), and on gqa_prefill
+    (B 1, S 8192, 32/4 heads, d_model 4096, headwise gate), where each group's
+    eight query heads are cut into slices whose float32 partial dK/dV sums are
+    added afterwards.  The oracle computes chosen key/value heads' dQ, dK, dV
+    (with every query head of their groups), their dW_θ columns (every token)
+    and a sample of dX rows exactly."""
     from helpers import sample_rows
-    cfg = CONFIGS["dense_prefill"]
+    cfg = CONFIGS[name]
     inp = make_inputs(cfg, seed=0, device=DEV)
     dY = make_grad(cfg, seed=0, device=DEV)
     out = run_backward(inp, dY, cfg.mode)
-    kv = [0, cfg.Hkv - 1]
+    kv = [0, cfg.Hkv - 1] if name == "dense_prefill" else [cfg.Hkv - 1]
     rows = sample_rows(cfg.S)
     ref = oracle.gated_sdpa_backward_sampled(f64(inp["X"]), f64(inp["W"]), f64(inp["Q"]), f64(inp["K"]),
                                              f64(inp["V"]), f64(dY), cfg.mode, kv, rows)
@@ -191,7 +196,7 @@ def test_backward_dense_prefill_full_size_sampled():
     }
     for n, got in pieces.items():
         want = ref[n]
-        report(got, want, bwd_tol(want), f"dense_prefill {n}")
+        report(got, want, bwd_tol(want), f"{name} {n}")
         rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
-        print(f"  dense_prefill {n}: rel_fro={rel:.3e}", flush=True)
+        print(f"  {name} {n}: rel_fro={rel:.3e}", flush=True)
         assert rel <= 1e-2
