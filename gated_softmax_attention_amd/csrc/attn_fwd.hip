@@ -250,28 +250,6 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
         for (int qb = 0; qb < QB; ++qb) s[sub][qb] = mfma32x32x16(a, qf[qb][kk], s[sub][qb]);
       }
   };
-  // Oᵀ += Vᵀ·Pᵀ from the V tile at vsrc; the D/32 output blocks are
-  // independent accumulation chains, interleaved
-  auto mma_pv = [&](const bf16* vsrc, const bf16x8 (&pb)[QB][2][2]) {
-    // an LDS pointer derived from the stage array (not from an integer), so
-    // the compiler keeps the provenance it needs for its alias information
-    GSA_LDS char* const vs = (GSA_LDS char*)(GSA_LDS void*)vsrc;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          GSA_LDS char* const a0 = vs + vt_base[dt] + (sub * 32 + 16 * t) * VSL * 16;
-          const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)a0);
-          const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(a0 + 8 * VSL * 16));
-          bf16x8 a;
-          a.lo = __builtin_bit_cast(bf16x4, lo);
-          a.hi = __builtin_bit_cast(bf16x4, hi);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma32x32x16(a, pb[qb][sub][t], o[qb][dt]);
-        }
-  };
   // Online softmax of one Sᵀ tile in two halves (the reference test between
   // them is the only branch of the loop body): row max in-lane, then across the
   // two wave halves, and the reference update; then p = exp2(s·c − m), P
@@ -324,33 +302,43 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     return __any(moved);
   };
-  // second half: p = exp2(s·c − m), P packed to bf16, row sum folded into l
-  auto softmax_exp = [&](f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2]) {
+  // second half, one 16-key quarter (sub, t) of the tile at a time: p =
+  // exp2(s·c − m), P packed to bf16 and summed into ps (l is updated once the
+  // four quarters are done), then that quarter's PV product, Oᵀ += Vᵀ·Pᵀ from
+  // the V tile at vsrc (the D/32 output blocks are independent accumulation
+  // chains).  A quarter's matrix ops depend only on its own probabilities, so
+  // the next quarter's exp work can run in their shadow; O still accumulates
+  // keys in increasing order.
+  auto exp_q = [&](f32x16 (&s)[2][QB], bf16x8 (&pb)[QB][2][2], float (&ps)[QB][2], int sub, int t) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float neg_m = -m_run[qb];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int e = 0; e < 8; ++e) s[sub][qb][8 * t + e] = fast_exp2(fmaf(s[sub][qb][8 * t + e], scale_log2, neg_m));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][qb][r] = fast_exp2(fmaf(s[sub][qb][r], scale_log2, neg_m));
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[qb][sub][t][e] = (bf16)s[sub][qb][8 * t + e];
+      for (int e = 0; e < 8; ++e) pb[qb][sub][t][e] = (bf16)s[sub][qb][8 * t + e];
       // l sums the bf16-rounded p, the very weights the PV product applies
-      float ps[2] = {0.f, 0.f};
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 pair = {pb[qb][sub][t][2 * w], pb[qb][sub][t][2 * w + 1]};
+        ps[qb][w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ps[qb][w & 1], false);
+      }
+    }
+  };
+  auto pv_q = [&](const bf16* vsrc, const bf16x8 (&pb)[QB][2][2], int sub, int t) {
+    // an LDS pointer derived from the stage array (not from an integer), so
+    // the compiler keeps the provenance it needs for its alias information
+    GSA_LDS char* const vs = (GSA_LDS char*)(GSA_LDS void*)vsrc;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+    for (int dt = 0; dt < D / 32; ++dt) {
+      GSA_LDS char* const a0 = vs + vt_base[dt] + (sub * 32 + 16 * t) * VSL * 16;
+      const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)a0);
+      const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS i16x4*)(a0 + 8 * VSL * 16));
+      bf16x8 a;
+      a.lo = __builtin_bit_cast(bf16x4, lo);
+      a.hi = __builtin_bit_cast(bf16x4, hi);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const bf16x2 pair = {pb[qb][sub][t][2 * w], pb[qb][sub][t][2 * w + 1]};
-            ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ps[w & 1], false);
-          }
-      l_run[qb] = l_run[qb] * alpha[qb] + (ps[0] + ps[1]);
+      for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma32x32x16(a, pb[qb][sub][t], o[qb][dt]);
     }
   };
   auto rescale_o = [&]() {
@@ -402,8 +390,18 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     if (move) rescale_o();
     bf16x8 pb[QB][2][2];
-    softmax_exp(cur, pb);
-    mma_pv(v_cur, pb);
+    float ps[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ps[qb][0] = ps[qb][1] = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        exp_q(cur, pb, ps, sub, t);
+        pv_q(v_cur, pb, sub, t);
+      }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_run[qb] * alpha[qb] + (ps[qb][0] + ps[qb][1]);
     wait_dma_and_sync();
   };
 
