@@ -207,6 +207,206 @@ void bwd_gemm_kernel(const bf16* __restrict__ L, const bf16* __restrict__ R, Out
   }
 }
 
+// ---------------------------------------------------------------- large tiles
+// The same products on 256 (m) x 256 (n) x 64 (k) tiles for shapes whose
+// dimensions are all multiples of 256: 8 waves in a 2 (m) x 4 (n) grid, each
+// with a 128 x 64 block (eight 32x32 accumulators: six operand fragments feed
+// eight matrix ops per 16-wide k step), one workgroup per CU, two LDS stages
+// filled by 16-byte direct loads.
+//   k-contiguous operand: 256 rows x 8 chunks of 8 k + one pad slot (144-byte
+//     stride); the fragment (8 consecutive k of one row) is one 16-byte read.
+//   m/n-contiguous operand: 64 k rows x 32 chunks (512 bytes), chunk index XOR
+//     4·(k & 3); the fragment (8 consecutive k of one column) comes from two
+//     transposed reads of 4 k rows each.
+// The fragments of k step s+1 are read while the matrix ops of step s run; a
+// stage's barrier sits before its last k step, so the next stage's first
+// reads overlap that step's matrix ops.  As in the small-tile kernel the
+// matrix op's row index is n, so each lane stores 4 consecutive outputs.
+namespace bgbig {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr uint32_t kOOB = 0xfffffff0u;
+template <bool KC>
+struct St {
+  static constexpr int SL = KC ? 9 : 32;              // 16-byte slots per LDS row
+  static constexpr int SLOTS = KC ? 256 * 9 : 64 * 32;
+  static constexpr int INS = SLOTS / 64;              // direct-load instructions per stage
+  static constexpr int PER_WAVE = (INS + 7) / 8;      // per wave (the last round may be partial)
+  static constexpr int BYTES = SLOTS * 16;
+};
+// one operand's direct loads: slot (wave + 8j)*64 + lane of the stage
+template <bool KC>
+struct BigLoader {
+  using S_ = St<KC>;
+  uint32_t off[S_::PER_WAVE];   // byte offset within the tile at k0 = 0, or kOOB
+  __device__ void init(int wave, int lane, int mn0, uint32_t ld) {
+#pragma unroll
+    for (int j = 0; j < S_::PER_WAVE; ++j) {
+      const int slot = (wave + 8 * j) * 64 + lane;
+      if (KC) {
+        const int row = slot / 9, c = slot % 9;
+        off[j] = (slot < S_::SLOTS && c < 8) ? ((uint32_t)(mn0 + row) * ld + 8u * c) * 2u : kOOB;
+      } else {
+        const int row = slot / 32, p = slot % 32, c = p ^ (4 * (row & 3));
+        off[j] = slot < S_::SLOTS ? ((uint32_t)row * ld + (uint32_t)(mn0 + 8 * c)) * 2u : kOOB;
+      }
+    }
+  }
+  // stage at k0 (k0 >= k_end: every slot reads zeros)
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t pad, int k0, int k_end, uint32_t ld,
+                       int wave) const {
+    const bool live = k0 < k_end;
+    const uint32_t kofs = KC ? (uint32_t)k0 * 2u : (uint32_t)k0 * ld * 2u;
+#pragma unroll
+    for (int j = 0; j < S_::PER_WAVE; ++j) {
+      const int ins = wave + 8 * j;
+      const bool real = ins < S_::INS;
+      dma16_lds(rs, (live && off[j] != kOOB) ? off[j] + kofs : kOOB, real ? lds + (uint32_t)ins * 1024u : pad);
+    }
+  }
+};
+// lane part of a fragment address for the 32-wide block starting at col0
+template <bool KC>
+__device__ __forceinline__ uint32_t big_frag_base(int lane, int col0) {
+  if (KC) {
+    return (uint32_t)(((col0 + (lane & 31)) * 9 + (lane >> 5)) * 16);
+  } else {
+    const int g = lane >> 4, si = lane & 15;
+    const int n = col0 + 16 * (g & 1) + 4 * (si & 3);
+    const int krow = 8 * (g >> 1) + (si >> 2);
+    const int phys = (n >> 3) ^ (4 * (krow & 3));
+    return (uint32_t)((krow * 32 + phys) * 16 + (n & 7) * 2);
+  }
+}
+// fragment of k step ks (k = 16 ks + 8 hl .. +7) at a lane base
+template <bool KC>
+__device__ __forceinline__ bf16x8 big_frag(const GSA_LDS_G char* tile, uint32_t base, int ks) {
+  if (KC) {
+    return *(const GSA_LDS_G bf16x8*)(tile + base + ks * 32);
+  } else {
+    const GSA_LDS_G char* p = tile + base + ks * 16 * 32 * 16;
+    bf16x8 a;
+    a.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_G i16x4*)p));
+    a.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GSA_LDS_G i16x4*)(p + 4 * 32 * 16)));
+    return a;
+  }
+}
+}  // namespace bgbig
+
+template <typename OutT, bool L_KC, bool R_KC>
+__global__ __launch_bounds__(512, 1)
+void bwd_gemm_big_kernel(const bf16* __restrict__ L, const bf16* __restrict__ R, OutT* __restrict__ out,
+                         int M, int N, uint32_t ldl, uint32_t ldr, uint32_t l_bytes, uint32_t r_bytes,
+                         int tiles_m, int tiles_n, int k_chunk) {
+  using namespace bgbig;
+  __shared__ __align__(16) char Ls[2][St<L_KC>::BYTES];
+  __shared__ __align__(16) char Rs[2][St<R_KC>::BYTES];
+  // landing area of the load rounds past a stage's last instruction
+  __shared__ __align__(16) char Pad[1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles = tiles_m * tiles_n;
+  const int z = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int tm = t / tiles_n, tn = t % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = z * k_chunk, ke = kb + k_chunk;
+  OutT* outz = out + (int64_t)z * M * N;
+
+  const auto lrs = make_rsrc(L, l_bytes);
+  const auto rrs = make_rsrc(R, r_bytes);
+  BigLoader<L_KC> lld;
+  BigLoader<R_KC> rld;
+  lld.init(wave, lane, m0, ldl);
+  rld.init(wave, lane, n0, ldr);
+  const uint32_t pad = __builtin_amdgcn_readfirstlane(lds_addr(&Pad[0]));
+  auto dma = [&](int k0, int buf) {
+    lld.load(lrs, __builtin_amdgcn_readfirstlane(lds_addr(&Ls[buf][0])), pad, k0, ke, ldl, wave);
+    rld.load(rrs, __builtin_amdgcn_readfirstlane(lds_addr(&Rs[buf][0])), pad, k0, ke, ldr, wave);
+  };
+  uint32_t lb[4], rb[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lb[i] = big_frag_base<L_KC>(lane, wm * 128 + 32 * i);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) rb[i] = big_frag_base<R_KC>(lane, wn * 64 + 32 * i);
+
+  f32x16 acc[2][4];   // [n block][m block]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  struct Frag {
+    bf16x8 l[4], r[2];
+  };
+  auto load_frag = [&](int buf, int ks, Frag& f) {
+    const GSA_LDS_G char* lt = (const GSA_LDS_G char*)(GSA_LDS_G void*)&Ls[buf][0];
+    const GSA_LDS_G char* rt = (const GSA_LDS_G char*)(GSA_LDS_G void*)&Rs[buf][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.l[i] = big_frag<L_KC>(lt, lb[i], ks);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.r[i] = big_frag<R_KC>(rt, rb[i], ks);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.r[i], f.l[j], acc[i][j]);
+  };
+
+  const int nk = k_chunk / BK;
+  static_assert(BK / 16 == 4, "four k steps per stage");
+  dma(kb, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  dma(kb + BK, 1);
+  Frag f0, f1;
+  load_frag(0, 0, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    load_frag(buf, 1, f1);
+    mma(f0);
+    load_frag(buf, 2, f0);
+    mma(f1);
+    load_frag(buf, 3, f1);
+    mma(f0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma(kb + (kt + 2) * BK, buf);     // past the chunk: zero rounds
+    load_frag(buf ^ 1, 0, f0);        // on the last stage: stale, unused
+    mma(f1);
+  }
+
+  // lane holds output row m0 + wm*128 + 32*j + l32 and columns
+  // n0 + wn*64 + 32*i + 8*(r/4) + 4*hl + 0..3
+  const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + 32 * j + l32;
+    OutT* orow = outz + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + 32 * i + 8 * q + 4 * hl;
+        const f32x16& c = acc[i][j];
+        if constexpr (std::is_same<OutT, float>::value) {
+          *(f32x4*)(orow + n) = f32x4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+        } else {
+          *(u32x2*)(orow + n) = u32x2{pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3])};
+        }
+      }
+  }
+}
+
+// Whether the large-tile kernel takes a backward GEMM: every dimension a
+// multiple of 256 and every operand addressable with 32-bit byte offsets.
+static bool bwd_big_ok(int64_t M, int64_t d_model, int64_t N) {
+  return M % 256 == 0 && d_model % 256 == 0 && N % 256 == 0 && M * N * 2 < (int64_t(1) << 31) &&
+         M * d_model * 2 < (int64_t(1) << 31) && d_model * N * 2 < (int64_t(1) << 31);
+}
+
 // out[i] = Σ_z part[z][i] in z order (float4 granules; n4 = element count / 4).
 __global__ __launch_bounds__(256)
 void sum_partials_kernel(const f32x4* __restrict__ part, f32x4* __restrict__ out, int64_t n4, int splits) {
@@ -220,6 +420,13 @@ void sum_partials_kernel(const f32x4* __restrict__ part, f32x4* __restrict__ out
 // Token chunks for dW_θ: enough workgroups to fill the chip (about 1024), each
 // chunk a multiple of 64 tokens and at least 256 of them.
 int64_t bwd_dw_splits(int64_t M, int64_t d_model, int64_t N) {
+  if (bwd_big_ok(M, d_model, N)) {
+    // large tiles: about one workgroup per CU, chunks a multiple of 256 tokens
+    const int64_t tiles = (d_model / 256) * (N / 256);
+    int64_t s = std::max<int64_t>(1, 256 / tiles);
+    while (s > 1 && (M % (256 * s) != 0)) --s;
+    return s;
+  }
   const int64_t tiles = ceil_div<int64_t>(d_model, bgemm::BM) * ceil_div<int64_t>(N, bgemm::BN);
   int64_t s = ceil_div<int64_t>(1024, tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, M / 256));
@@ -232,6 +439,13 @@ int64_t bwd_dw_chunk(int64_t M, int64_t splits) {
 // dX[M, d_model] = dZ[M, N] · W_θ[d_model, N]ᵀ  (both operands k-contiguous, k = N)
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
                               int64_t N, hipStream_t st) {
+  if (bwd_big_ok(M, d_model, N)) {
+    const int tm = (int)(M / 256), tn = (int)(d_model / 256);
+    hipLaunchKernelGGL((bwd_gemm_big_kernel<bf16, true, true>), dim3((unsigned)(tm * tn)), dim3(512), 0, st,
+                       (const bf16*)dZ, (const bf16*)W, (bf16*)dX, (int)M, (int)d_model, (uint32_t)N,
+                       (uint32_t)N, (uint32_t)(M * N * 2), (uint32_t)(d_model * N * 2), tm, tn, (int)N);
+    return hipGetLastError();
+  }
   const int tm = (int)ceil_div<int64_t>(M, bgemm::BM), tn = (int)ceil_div<int64_t>(d_model, bgemm::BN);
   hipLaunchKernelGGL((bwd_gemm_kernel<bf16, true, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, st,
                      (const bf16*)dZ, (const bf16*)W, (bf16*)dX, (int)M, (int)d_model, (int)N,
@@ -244,13 +458,21 @@ hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M
 // partials: splits * d_model * N floats when splits > 1 (else unused)
 hipError_t launch_bwd_gemm_dw(const void* X, const void* dZ, float* dW, float* partials, int64_t M,
                               int64_t d_model, int64_t N, int64_t splits, hipStream_t st) {
+  float* dst = splits > 1 ? partials : dW;
+  if (bwd_big_ok(M, d_model, N)) {
+    const int tm = (int)(d_model / 256), tn = (int)(N / 256);
+    hipLaunchKernelGGL((bwd_gemm_big_kernel<float, false, false>), dim3((unsigned)(tm * tn * splits)), dim3(512),
+                       0, st, (const bf16*)X, (const bf16*)dZ, dst, (int)d_model, (int)N, (uint32_t)d_model,
+                       (uint32_t)N, (uint32_t)(M * d_model * 2), (uint32_t)(M * N * 2), tm, tn,
+                       (int)(M / splits));
+  } else {
   const int tm = (int)ceil_div<int64_t>(d_model, bgemm::BM), tn = (int)ceil_div<int64_t>(N, bgemm::BN);
   const int64_t chunk = bwd_dw_chunk(M, splits);
-  float* dst = splits > 1 ? partials : dW;
   hipLaunchKernelGGL((bwd_gemm_kernel<float, false, false>), dim3((unsigned)(tm * tn * splits)), dim3(256), 0,
                      st, (const bf16*)X, (const bf16*)dZ, dst, (int)d_model, (int)N, (int)M,
                      (uint32_t)d_model, (uint32_t)N, (uint32_t)(M * d_model * 2), (uint32_t)(M * N * 2), tm,
                      tn, (int)chunk);
+  }
   if (splits > 1) {
     const int64_t n4 = d_model * N / 4;
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div<int64_t>(n4, 256), 4096);

@@ -103,6 +103,16 @@ def test_backward_gate_widths(dm, mode):
     check_against_oracle(inp, dY, mode, f"dm{dm} {mode}")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,D,dm", [(512, 2, 2, 128, 512), (1024, 4, 2, 64, 256)])
+def test_backward_large_tile_gemms(S, Hq, Hkv, D, dm):
+    """Token count, d_model and gate width all multiples of 256: dX and dW_θ take
+    the 256 x 256 tile products, dW_θ with 2 and 4 token chunks of partial sums."""
+    cfg = small_cfg(1, S, Hq, Hkv, D, "elementwise", dm=dm)
+    inp = make_inputs(cfg, seed=S + dm, device=DEV)
+    dY = make_grad(cfg, seed=S + dm, device=DEV)
+    check_against_oracle(inp, dY, "elementwise", f"S{S} {Hq}/{Hkv} D{D} dm{dm}")
+
+
 def test_backward_rejects_unsupported():
     cfg = small_cfg(1, 16, 4, 4, 64, "headwise")          # headwise gate width 4: not a multiple of 8
     inp = make_inputs(cfg, seed=1, device=DEV)
