@@ -306,7 +306,11 @@ void bwd_gemm_big_kernel(const bf16* __restrict__ L, const bf16* __restrict__ R,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int tiles = tiles_m * tiles_n;
-  const int z = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int z = blockIdx.x / tiles, t0 = blockIdx.x % tiles;
+  // workgroup ids are dealt round-robin over the 8 XCDs: XCD x = id % 8 takes
+  // the x-th contiguous eighth of the row-major tile list, so an L row block
+  // is fetched into one L2 instead of all eight
+  const int t = tiles % 8 == 0 ? (t0 % 8) * (tiles / 8) + t0 / 8 : t0;
   const int tm = t / tiles_n, tn = t % tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb = z * k_chunk, ke = kb + k_chunk;
