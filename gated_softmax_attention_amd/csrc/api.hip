@@ -27,7 +27,7 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
                            int mode, hipStream_t stream);
-int bwd_kv_slices(int B, int S, int Hq, int Hkv);
+int bwd_kv_slices(int B, int S, int Hq, int Hkv, int D);
 hipError_t launch_project_qkvg(const void* X, const void* W, void* Q, void* Kp, void* V, float* G, int64_t M,
                                int64_t K, int64_t nq, int64_t nkv, int64_t ng, hipStream_t stream);
 hipError_t launch_attn_fwd_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
@@ -288,7 +288,7 @@ BwdLayout bwd_layout(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, i
   if (gated) off += align256((size_t)(M * N) * 2);
   l.part = off;
   size_t part = 0;
-  const int64_t ns = gsa::bwd_kv_slices((int)B, (int)S, (int)Hq, (int)Hkv);
+  const int64_t ns = gsa::bwd_kv_slices((int)B, (int)S, (int)Hq, (int)Hkv, (int)D);
   if (ns > 1) part = (size_t)(2 * ns * M * Hkv * D) * 4;
   if (gated) {
     l.splits = gsa::bwd_dw_splits(M, d_model, N);

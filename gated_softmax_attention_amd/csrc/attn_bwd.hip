@@ -34,7 +34,7 @@ namespace gsa {
 namespace bwd {
 constexpr int QT = 128;   // query rows per dQ workgroup (4 waves x 32)
 constexpr int KT = 64;    // key rows per staged tile in the dQ kernel
-constexpr int KW = 128;   // key rows per dK/dV workgroup (4 waves x 32)
+constexpr int KW = 128;   // key rows per dK/dV workgroup at D = 64 (4 waves x 32)
 constexpr int QW = 64;    // query rows per staged tile in the dK/dV kernel
 constexpr uint32_t kOOB = 0xfffffff0u;
 }  // namespace bwd
@@ -144,23 +144,23 @@ struct Tile {
   static __device__ __forceinline__ int chunk_off(int row, int c) { return (SWZ ? c ^ tile_swz(row) : c) * 16; }
 };
 
-// Direct loads of `rows` rows of a [*, stride] bf16 tensor into a tile: 4
-// waves, wave instruction i covers slots 64*i .. 64*i+63 (slot s = row·SL +
+// Direct loads of `rows` rows of a [*, stride] bf16 tensor into a tile by
+// WAVES waves; instruction i covers slots 64*i .. 64*i+63 (slot s = row·SL +
 // physical chunk).  Rows at or past `row_end` and the pad slot read zeros.
 // Every instruction writes all 64 slots, so the LDS buffer must hold kBytes
 // (whole instructions), which exceeds ROWS row strides when ROWS * SL is not a
 // multiple of 64.
-template <int D, int ROWS>
+template <int D, int ROWS, int WAVES = 4>
 struct TileLoader {
   static constexpr int SL = Tile<D>::SL;
-  static constexpr int NI = (ROWS * SL + 255) / 256;   // instructions per wave
+  static constexpr int NI = (ROWS * SL + 64 * WAVES - 1) / (64 * WAVES);   // instructions per wave
   static constexpr int kBytes = (ROWS * SL + 63) / 64 * 1024;
   uint32_t off[NI];
   uint32_t ins_base[NI];
   __device__ void init(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int ins = wave + 4 * j;
+      const int ins = wave + WAVES * j;
       const int sl = ins * 64 + lane;
       const int row = sl / SL, ch = sl % SL;
       // the logical chunk stored in physical slot ch (the swizzle is its own inverse)
@@ -176,7 +176,7 @@ struct TileLoader {
     const uint32_t base = (uint32_t)r0 * row_bytes;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int ins = wave + 4 * j;
+      const int ins = wave + WAVES * j;
       if (ins * 64 < ROWS * SL) {
         const int lane_row = (int)((ins_base[j] / 16 + (threadIdx.x & 63)) / SL);
         const bool ok = off[j] != kOOBv() && r0 + lane_row < row_end;
@@ -570,16 +570,18 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 }
 
 // ---------------------------------------------------------------- dK, dV at D = 128
-// The same products as bwd_dkdv_kernel, arranged to fit two workgroups per CU
-// (≤ 256 registers, 72 KB of LDS each) so one workgroup's waves cover the
-// other's LDS and barrier waits:
-//   * V of the workgroup's 128 keys is staged once in LDS and read back as the
+// The same products as bwd_dkdv_kernel, arranged to fit two waves per SIMD
+// (≤ 256 registers): WAVES = 4 runs two workgroups per CU (66 KB of LDS
+// each), so one workgroup's waves cover the other's LDS and barrier waits;
+// WAVES = 8 runs one workgroup of 256 keys per CU (98 KB), in which each
+// staged query tile feeds twice the matrix ops.
+//   * V of the workgroup's keys is staged once in LDS and read back as the
 //     B operand of dP (a 16-byte row read per k step) instead of living in
 //     registers;
 //   * query tiles are 32 rows, halving the S and dP accumulators.
 // K fragments and the dK/dV accumulators stay in registers.
-template <int D, bool PARTIAL>
-__global__ __launch_bounds__(256, 2)
+template <int D, bool PARTIAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES)
 void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                           const bf16* __restrict__ dY, const float* __restrict__ Stat,
                           bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKp,
@@ -587,9 +589,10 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
                           float scale) {
   using namespace bwd;
   constexpr int RSB = Tile<D>::RSB;
-  constexpr int QR = 32;   // query rows per staged tile
-  constexpr int QB = TileLoader<D, QR>::kBytes;   // 32 rows, rounded up to whole loads
-  __shared__ __align__(16) char Vt[TileLoader<D, KW>::kBytes];
+  constexpr int QR = 32;                 // query rows per staged tile
+  constexpr int KWV = 32 * WAVES;        // keys per workgroup
+  constexpr int QB = TileLoader<D, QR, WAVES>::kBytes;   // 32 rows, rounded up to whole loads
+  __shared__ __align__(16) char Vt[TileLoader<D, KWV, WAVES>::kBytes];
   __shared__ __align__(16) char Qs[2][QB];
   __shared__ __align__(16) char Ys[2][QB];
   __shared__ __align__(16) float Ss[2][256];   // per stage: base-2 LSE of 32 rows, D of 32 rows, pad
@@ -603,7 +606,7 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int slice = rest % nsplit, pair = rest / nsplit;
   const int kvh = pair % Hkv, b = pair / Hkv;
   const int G = Hq / Hkv, Gs = G / nsplit;
-  const int k0 = kt_i * KW, kw0 = k0 + wave * 32, my_k = kw0 + l32;
+  const int k0 = kt_i * KWV, kw0 = k0 + wave * 32, my_k = kw0 + l32;
   const int64_t q_row = (int64_t)Hq * D, kv_row = (int64_t)Hkv * D;
   const float scale_log2 = scale * kLog2e;
 
@@ -611,7 +614,7 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const uint32_t kv_row_b = (uint32_t)(kv_row * 2);
   const auto vr = make_rsrc(V + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
   {
-    TileLoader<D, KW> vld;
+    TileLoader<D, KWV, WAVES> vld;
     vld.init(wave, lane, kv_row_b);
     vld.load(vr, kv_row_b, k0, S, __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0])), wave);
   }
@@ -627,7 +630,7 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]));
   }
   const uint32_t row_b = (uint32_t)(q_row * 2);
-  TileLoader<D, QR> ld;
+  TileLoader<D, QR, WAVES> ld;
   ld.init(wave, lane, row_b);
   uint32_t qs_lds[2], ys_lds[2], st_lds[2];
 #pragma unroll
@@ -652,7 +655,7 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       dv[dt][r] = 0.f;
     }
 
-  // query tiles that see keys [k0, k0 + KW): rows >= k0
+  // query tiles that see keys [k0, k0 + KWV): rows >= k0
   const int qt_first = k0 / QR;
   const int n_qt = ceil_div(S, QR) - qt_first;
   const int n_steps = Gs * max(n_qt, 0);
@@ -778,13 +781,23 @@ void bwd_sum_slices_kernel(const f32x4* __restrict__ dKp, const f32x4* __restric
 }
 
 // ---------------------------------------------------------------- launch
+// Waves (32 keys each) per dK/dV workgroup.  At D = 128 and S >= 8192 one
+// eight-wave workgroup per CU (256 keys) halves the query-tile loads per
+// matrix op and doubles the time each tile's loads have to arrive (1-2%
+// faster there); on shorter sequences its workgroups are short and nothing
+// covers one's prologue, so two four-wave workgroups per CU are faster.
+static int bwd_dkdv_waves(int S, int D) { return D == 128 && S >= 8192 ? 8 : 4; }
+
 // Query-head slices per key/value head for the dK/dV kernel: the smallest
-// divisor of the group size that gives about 1024 workgroups.
-int bwd_kv_slices(int B, int S, int Hq, int Hkv) {
+// divisor of the group size that gives about 1024 four-wave workgroups (or
+// the same number of waves in eight-wave ones).
+int bwd_kv_slices(int B, int S, int Hq, int Hkv, int D) {
   const int G = Hq / Hkv;
-  const int64_t base = (int64_t)ceil_div(S, bwd::KW) * Hkv * B;
+  const int waves = bwd_dkdv_waves(S, D);
+  const int64_t base = (int64_t)ceil_div(S, 32 * waves) * Hkv * B;
+  const int64_t target = 4096 / waves;
   for (int ns = 1; ns < G; ++ns)
-    if (G % ns == 0 && base * ns >= 1024) return ns;
+    if (G % ns == 0 && base * ns >= target) return ns;
   return G;
 }
 int bwd_stat_rows(int S) { return ceil_div(S, 64) * 64; }
@@ -815,17 +828,23 @@ static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, cons
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((int64_t)nq * Hq * B)), dim3(256), 0, st,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, (bf16*)dQ,
                      B, S, Hq, Hkv, nq, Sp, scale);
-  const int nk = ceil_div(S, bwd::KW);
-  const int ns = bwd_kv_slices(B, S, Hq, Hkv);
-  const unsigned grid = (unsigned)((int64_t)nk * Hkv * B * ns);
   constexpr bool vlds = D == 128;
+  const int waves = bwd_dkdv_waves(S, D);
+  const int nk = ceil_div(S, 32 * waves);
+  const int ns = bwd_kv_slices(B, S, Hq, Hkv, D);
+  const unsigned grid = (unsigned)((int64_t)nk * Hkv * B * ns);
   auto dkdv = [&](auto partial, bf16* dk, bf16* dv, float* dkp, float* dvp) {
     constexpr bool P = decltype(partial)::value;
-    if constexpr (vlds)
-      hipLaunchKernelGGL((bwd_dkdv_vlds_kernel<D, P>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
-                         (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
-                         Hq, Hkv, Sp, ns, scale);
-    else
+    if constexpr (vlds) {
+      if (waves == 8)
+        hipLaunchKernelGGL((bwd_dkdv_vlds_kernel<D, P, 8>), dim3(grid), dim3(512), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
+                           Hq, Hkv, Sp, ns, scale);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_vlds_kernel<D, P, 4>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
+                           Hq, Hkv, Sp, ns, scale);
+    } else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, P>), dim3(grid), dim3(256), 0, st, (const bf16*)Q,
                          (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, dk, dv, dkp, dvp, B, S,
                          Hq, Hkv, Sp, ns, scale);

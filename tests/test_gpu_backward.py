@@ -113,6 +113,17 @@ def test_backward_large_tile_gemms(S, Hq, Hkv, D, dm):
     check_against_oracle(inp, dY, "elementwise", f"S{S} {Hq}/{Hkv} D{D} dm{dm}")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv", [(8192, 2, 2), (8200, 2, 1)])
+def test_backward_long_rows(S, Hq, Hkv):
+    """S >= 8192 at D = 128: dK/dV run in eight-wave workgroups of 256 keys,
+    whole groups (S 8192, MHA) and sliced ones with float32 partials and a
+    ragged last key tile (S 8200, two query heads per key/value head)."""
+    cfg = small_cfg(1, S, Hq, Hkv, 128, "elementwise")
+    inp = make_inputs(cfg, seed=S, device=DEV)
+    dY = make_grad(cfg, seed=S, device=DEV)
+    check_against_oracle(inp, dY, "elementwise", f"S{S} {Hq}/{Hkv} D128")
+
+
 def test_backward_rejects_unsupported():
     cfg = small_cfg(1, 16, 4, 4, 64, "headwise")          # headwise gate width 4: not a multiple of 8
     inp = make_inputs(cfg, seed=1, device=DEV)
