@@ -346,22 +346,24 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
         for (int r = 0; r < 16; ++r)
           if (sub * 32 + 8 * (r >> 2) + (r & 3) > lim) s[sub][r] = -INFINITY;
     }
+    // dS and the dQ product one 16-key quarter (sub, t) at a time: a quarter's
+    // matrix ops need only its own dS, so the next quarter's exp work runs in
+    // their shadow (dQ still accumulates keys in increasing order)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[sub][r], scale_log2, -lse2));
-        s[sub][r] = p * (dp[sub][r] - dval);   // dS
-      }
-    bf16x8 ds[2][2];
-    pack_b(s, ds);
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 ds;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * t + e;
+          const float p = fast_exp2(fmaf(s[sub][r], scale_log2, -lse2));
+          ds[e] = (bf16)(p * (dp[sub][r] - dval));   // dS
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-          acc[dt] = mfma32x32x16(tr_read(kt + (sub * 32 + 16 * t) * RSB, trb[dt]), ds[sub][t], acc[dt]);
+          acc[dt] = mfma32x32x16(tr_read(kt + (sub * 32 + 16 * t) * RSB, trb[dt]), ds, acc[dt]);
+      }
   }
 
   if (my_q >= S) return;
@@ -712,35 +714,32 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
         if (off < lo || off > hi) s[r] = -INFINITY;
       }
     }
+    // P, dS and the dV / dK products one 16-row half t at a time: a half's
+    // matrix ops need only its own P and dS, so the next half's exp work runs
+    // in their shadow (dV and dK still accumulate rows in increasing order)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row4 = 8 * i + 4 * hl;
-      const f32x4 l4 = *(const GSA_LDS_B f32x4*)(st + row4);
-      const f32x4 d4 = *(const GSA_LDS_B f32x4*)(st + QR + row4);
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 pb, db;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * i + j;
-        const float p = fast_exp2(fmaf(s[r], scale_log2, -l4[j]));
-        dp[r] = p * (dp[r] - d4[j]);   // dS
-        s[r] = p;
+      for (int i = 2 * t; i < 2 * t + 2; ++i) {
+        const int row4 = 8 * i + 4 * hl;
+        const f32x4 l4 = *(const GSA_LDS_B f32x4*)(st + row4);
+        const f32x4 d4 = *(const GSA_LDS_B f32x4*)(st + QR + row4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          const float p = fast_exp2(fmaf(s[r], scale_log2, -l4[j]));
+          pb[r - 8 * t] = (bf16)p;
+          db[r - 8 * t] = (bf16)(p * (dp[r] - d4[j]));   // dS
+        }
       }
-    }
-    bf16x8 pb[2], db[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[t][e] = (bf16)s[8 * t + e];
-        db[t][e] = (bf16)dp[8 * t + e];
-      }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int ro = 16 * t * RSB;
-        dv[dt] = mfma32x32x16(tr_read(yt + ro, trb[dt]), pb[t], dv[dt]);
-        dk[dt] = mfma32x32x16(tr_read(qt + ro, trb[dt]), db[t], dk[dt]);
+        dv[dt] = mfma32x32x16(tr_read(yt + ro, trb[dt]), pb, dv[dt]);
+        dk[dt] = mfma32x32x16(tr_read(qt + ro, trb[dt]), db, dk[dt]);
       }
+    }
   }
 
   if (my_k >= S) return;
