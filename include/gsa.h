@@ -44,7 +44,7 @@ typedef enum gsa_status {
   GSA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, Hq % Hkv != 0, mode/G mismatch */
   GSA_ERR_UNSUPPORTED = 2,   /* a head dim, dtype, mode or device the library does not handle */
   GSA_ERR_MISALIGNED = 3,    /* a pointer not 16-byte aligned */
-  GSA_ERR_WORKSPACE = 4,     /* decode workspace missing or smaller than required */
+  GSA_ERR_WORKSPACE = 4,     /* decode or backward workspace missing or smaller than required */
   GSA_ERR_NO_DEVICE = 5,     /* no HIP device visible to the calling thread */
   GSA_ERR_HIP = 6            /* a HIP runtime or kernel-launch error */
 } gsa_status;
