@@ -13,8 +13,10 @@ def f64(t):
     return to_float64_numpy(t)
 
 
-def report(got, want, tol, what=""):
-    """Assert max |got - want| <= tol (NaN in got fails); print max / mean / worst index."""
+def report(got, want, tol, what="", rel=0.0):
+    """Assert |got - want| <= tol + rel·|want| elementwise (NaN in got fails);
+    print max / mean / worst index.  rel covers a final rounding of the result
+    itself, whose error grows with the element's magnitude."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
@@ -24,9 +26,12 @@ def report(got, want, tol, what=""):
         raise AssertionError(f"{what}: NaN at {idx}")
     mx = float(err.max()) if err.size else 0.0
     mean = float(err.mean()) if err.size else 0.0
-    idx = np.unravel_index(int(np.argmax(err)), err.shape) if err.size else ()
+    over = err - rel * np.abs(want)
+    idx = np.unravel_index(int(np.argmax(over)), err.shape) if err.size else ()
+    worst = float(over[idx]) if err.size else 0.0
     print(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e} worst={idx}", flush=True)
-    assert mx <= tol, f"{what}: max_abs {mx:.3e} > {tol:.1e} at {idx} (got {got[idx]}, want {want[idx]})"
+    assert worst <= tol, (f"{what}: |err| {err[idx]:.3e} > {tol:.1e} + {rel:.2e}*|ref| at {idx} "
+                          f"(got {got[idx]}, want {want[idx]})")
     return mx
 
 

@@ -42,9 +42,14 @@ def test_forward_lse(B, S, Hq, Hkv, D, mode, dtype):
 # --------------------------------------------------------------- gsa_backward vs the oracle
 def bwd_tol(ref):
     """The bf16 bar (2e-2 max-abs) scaled by the gradient's RMS when that exceeds 1:
-    every bf16 rounding on the way (g·dY', P, dS, dZ and the output) is relative."""
+    every bf16 rounding on the way (g·dY', P, dS, dZ and the output) is relative.
+    Used with BWD_REL: an element far above the RMS also carries the RNE
+    rounding of its own bf16 output, up to 2^-8 of its magnitude."""
     rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
     return TOL["bf16"] * max(1.0, rms)
+
+
+BWD_REL = 2.0 ** -8
 
 
 def run_backward(inp, dY, mode):
@@ -66,7 +71,7 @@ def check_against_oracle(inp, dY, mode, label):
     for n in names:
         want = ref[n]
         got = f64(out[n]).reshape(want.shape)
-        report(got, want, bwd_tol(want), f"{label} {n}")
+        report(got, want, bwd_tol(want), f"{label} {n}", rel=BWD_REL)
         nrm = float(np.linalg.norm(want))
         if nrm > 0:   # (a single key makes dQ exactly zero: then only the max-abs bar applies)
             rel = float(np.linalg.norm(got - want)) / nrm
@@ -217,7 +222,7 @@ def test_backward_full_size_sampled(name):
     }
     for n, got in pieces.items():
         want = ref[n]
-        report(got, want, bwd_tol(want), f"{name} {n}")
+        report(got, want, bwd_tol(want), f"{name} {n}", rel=BWD_REL)
         rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
         print(f"  {name} {n}: rel_fro={rel:.3e}", flush=True)
         assert rel <= 1e-2
