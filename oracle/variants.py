@@ -74,6 +74,9 @@ def gated_sdpa_variant(X, W, Q, K, V, mode, act="sigmoid", combine="mul", norm=N
     combine in {"mul", "add"}; norm in {None, "rms"}.  With mode "none" the
     result is the (optionally normalised) SDPA output.  With ``rows`` only
     those query rows are evaluated and returned ([B, len(rows), Hq, D]).
+    K and V may hold more keys than Q has rows (query i at position
+    i + Skv - S): one decode step is S = 1 against the whole cache, and the
+    gate then sits at the decode merge.
     """
     Q = np.asarray(Q, dtype=np.float64)
     B, S, Hq, D = Q.shape

@@ -20,10 +20,13 @@ def sig(z):
 
 
 def brute_variant(t, mode, act, combine, norm):
-    """Pure-Python loops: SDPA row, optional RMSNorm, activation, combine."""
+    """Pure-Python loops: SDPA row, optional RMSNorm, activation, combine.
+    K and V may hold Skv >= S keys: query i then sits at position i + Skv - S
+    (a decode step has S = 1 and sees every cached key)."""
     X, W, Q, K, V = (t[k] for k in "XWQKV")
     B, S, Hq, D = Q.shape
     G = Hq // K.shape[2]
+    off = K.shape[1] - S
     dm = X.shape[2]
     f = {"identity": lambda z: z, "sigmoid": sig, "ns_sigmoid": lambda z: 0.5 + 0.5 * sig(z),
          "silu": lambda z: z * sig(z)}[act]
@@ -32,11 +35,12 @@ def brute_variant(t, mode, act, combine, norm):
         for i in range(S):
             for h in range(Hq):
                 c = h // G
-                s = [math.fsum(Q[b, i, h, d] * K[b, j, c, d] for d in range(D)) / math.sqrt(D) for j in range(i + 1)]
+                s = [math.fsum(Q[b, i, h, d] * K[b, j, c, d] for d in range(D)) / math.sqrt(D)
+                     for j in range(i + off + 1)]
                 mx = max(s)
                 w = [math.exp(x - mx) for x in s]
                 tot = math.fsum(w)
-                y = [math.fsum(w[j] * V[b, j, c, d] for j in range(i + 1)) / tot for d in range(D)]
+                y = [math.fsum(w[j] * V[b, j, c, d] for j in range(i + off + 1)) / tot for d in range(D)]
                 if norm == "rms":
                     r = math.sqrt(math.fsum(v * v for v in y) / D + ov.RMS_EPS)
                     y = [v / r for v in y]
@@ -63,6 +67,30 @@ def test_matches_brute_force(mode, act, combine, norm):
     t = draw(np.random.default_rng(len(mode) + len(act)), B, S, Hq, Hkv, D, dm, N)
     got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
     assert np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12
+
+
+@pytest.mark.parametrize("mode,act,combine,norm", CASES)
+def test_decode_shape_matches_brute_force(mode, act, combine, norm):
+    """The same variants for one decode step: a single query per batch against a
+    cache of L keys that holds it (the gate at the decode merge)."""
+    B, L, Hq, Hkv, D, dm = 3, 7, 4, 2, 3, 4
+    N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+    rng = np.random.default_rng(7 + len(mode) + len(act))
+    t = draw(rng, B, L, Hq, Hkv, D, dm, N)
+    t["X"], t["Q"] = t["X"][:, -1:], t["Q"][:, -1:]          # the newest token queries the cache
+    got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
+    assert got.shape == (B, 1, Hq, D)
+    assert np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12
+
+
+def test_default_decode_variant_is_the_decode_oracle_bitwise():
+    rng = np.random.default_rng(11)
+    for mode, N in (("elementwise", 4 * 3), ("headwise", 4)):
+        t = draw(rng, 2, 9, 4, 2, 3, 5, N)
+        t["X"], t["Q"] = t["X"][:, -1:], t["Q"][:, -1:]
+        got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode)
+        want = oracle.gated_decode(t["X"], t["W"], t["Q"], t["K"], t["V"], mode)
+        assert np.array_equal(got, want), mode
 
 
 def test_activation_closed_forms():
