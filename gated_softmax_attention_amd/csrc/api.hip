@@ -28,6 +28,12 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const vo
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
                            int mode, hipStream_t stream);
 int bwd_kv_slices(int B, int S, int Hq, int Hkv, int D);
+hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                                      void* workspace, int B, int L, int Hq, int Hkv, int D, int layout, int add,
+                                      int rms, int nsplit, hipStream_t st);
+hipError_t launch_attn_fwd_variant_f32_decode(const void* Q, const void* K, const void* V, const float* G,
+                                              void* Y, int B, int L, int Hq, int Hkv, int D, int layout, int add,
+                                              int rms, hipStream_t stream);
 hipError_t launch_project_qkvg(const void* X, const void* W, void* Q, void* Kp, void* V, float* G, int64_t M,
                                int64_t K, int64_t nq, int64_t nkv, int64_t ng, hipStream_t stream);
 hipError_t launch_attn_fwd_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
@@ -258,6 +264,45 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
   return hip_result(gsa::launch_attn_fwd(Q, Kc, Vc, G, Y, nullptr, (int)B, 1, (int)L, (int)Hq, (int)Hkv, (int)D,
                                          mode, false, (hipStream_t)stream),
                     "gsa_decode launch");
+}
+
+gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
+                              int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int layout, int combine, int norm,
+                              int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gsa_decode_variant";
+  if (!Q || !Kc || !Vc || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (layout < GSA_GATE_NONE || layout > GSA_GATE_SHARED)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown gate layout %d", fn, layout);
+  if (combine != GSA_COMBINE_MUL && combine != GSA_COMBINE_ADD)
+    return fail(GSA_ERR_INVALID_ARG, "%s: unknown combine %d", fn, combine);
+  if (norm != GSA_NORM_NONE && norm != GSA_NORM_RMS) return fail(GSA_ERR_INVALID_ARG, "%s: unknown norm %d", fn, norm);
+  // the shape rules of gsa_decode, with the shared layout checked as a gate
+  if (gsa_status st = check_attn_shape(fn, B, L, Hq, Hkv, D,
+                                       layout == GSA_GATE_SHARED ? GSA_GATE_ELEMENTWISE : layout, G, 1))
+    return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "%s: Q, Kc, Vc, G and Y must be 16-byte aligned", fn);
+  int64_t ns = 0;
+  if (dtype == GSA_BF16) {
+    ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+    const size_t need = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(GSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+    if (workspace && !aligned16(workspace)) return fail(GSA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+  }
+  if (gsa_status st = check_device()) return st;
+  const int add = combine == GSA_COMBINE_ADD, rms = norm == GSA_NORM_RMS;
+  if (dtype == GSA_BF16)
+    return hip_result(gsa::launch_decode_variant_bf16(Q, Kc, Vc, G, Y, workspace, (int)B, (int)L, (int)Hq,
+                                                      (int)Hkv, (int)D, layout, add, rms, (int)ns,
+                                                      (hipStream_t)stream),
+                      fn);
+  return hip_result(gsa::launch_attn_fwd_variant_f32_decode(Q, Kc, Vc, G, Y, (int)B, (int)L, (int)Hq, (int)Hkv,
+                                                            (int)D, layout, add, rms, (hipStream_t)stream),
+                    fn);
 }
 
 namespace {

@@ -282,6 +282,54 @@ void decode_merge_bf16_kernel(const float* __restrict__ part, const float* __res
   Y[((int64_t)b * Hq + h) * D + d] = (bf16)y;
 }
 
+// Design-space epilogue of the merge ("GatedAttention [2025]" §1.2.2 items
+// (3)-(5), §1.4.1 RMSNorm): layout 0 none, 1 elementwise (gate column h·D + d),
+// 2 headwise (column h), 3 head-shared (column d); add: Y + g instead of Y ⊙ g;
+// rms: the merged head output is first divided by sqrt(mean_d y² + ε) (unit
+// weight, ε = 1e-6).  G holds already-activated gate values, [B, N].
+struct DecEpi {
+  int layout, add, rms;
+};
+constexpr float kDecRmsEps = 1e-6f;
+
+template <int D>
+__global__ __launch_bounds__(D)
+void decode_merge_variant_bf16_kernel(const float* __restrict__ part, const float* __restrict__ Gate,
+                                      bf16* __restrict__ Y, int Hq, int nsplit, DecEpi ep) {
+  constexpr int PST = D + 4;
+  __shared__ float red[D / 64];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const float* p = part + ((int64_t)b * Hq + h) * nsplit * PST;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * PST + D]);
+  float lsum = 0.f, osum = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = fast_exp2(p[s * PST + D] - M);
+    lsum += p[s * PST + D + 1] * f;
+    osum += p[s * PST + d] * f;
+  }
+  float y = osum / lsum;
+  if (ep.rms) {
+    // sum of squares over the head's D values: each wave, then the waves in order
+    float ss = y * y;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((d & 63) == 0) red[d >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) tot += red[w];
+    y *= 1.0f / sqrtf(tot / (float)D + kDecRmsEps);
+  }
+  if (ep.layout != kDecGateNone) {
+    const float g = ep.layout == kDecGateElem ? Gate[((int64_t)b * Hq + h) * D + d]
+                    : ep.layout == kDecGateHead ? Gate[(int64_t)b * Hq + h]
+                                                : Gate[(int64_t)b * D + d];
+    y = ep.add ? y + g : y * g;
+  }
+  Y[((int64_t)b * Hq + h) * D + d] = (bf16)y;
+}
+
 int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv) {
   const int64_t G = Hq / Hkv;
   const int64_t base = B * Hkv * ((G + 3) / 4);
@@ -319,6 +367,28 @@ static void launch_dec(const void* Q, const void* K, const void* V, const float*
   else
     hipLaunchKernelGGL((decode_merge_bf16_kernel<D, kDecGateNone>), dim3(Hq, B), dim3(D), 0, st,
                        (const float*)part, G, (bf16*)Y, Hq, nsplit);
+}
+
+hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                                      void* workspace, int B, int L, int Hq, int Hkv, int D, int layout, int add,
+                                      int rms, int nsplit, hipStream_t st) {
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  const int chunk = (int)decode_chunk(L, nsplit);
+  float* part = (float*)workspace;
+  const int nquad = (Hq / Hkv + 3) / 4;
+  const DecEpi ep{layout, add, rms};
+  if (D == 128) {
+    hipLaunchKernelGGL((decode_split_bf16_kernel<128>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<128>), dim3(Hq, B), dim3(128), 0, st, (const float*)part,
+                       G, (bf16*)Y, Hq, nsplit, ep);
+  } else {
+    hipLaunchKernelGGL((decode_split_bf16_kernel<64>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
+                       G, (bf16*)Y, Hq, nsplit, ep);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,

@@ -692,4 +692,16 @@ hipError_t launch_attn_fwd_variant(const void* Q, const void* K, const void* V, 
   return hipGetLastError();
 }
 
+// float32 decode with a design-space epilogue: one query row per batch aligned
+// to the end of the L-long cache
+hipError_t launch_attn_fwd_variant_f32_decode(const void* Q, const void* K, const void* V, const float* G,
+                                              void* Y, int B, int L, int Hq, int Hkv, int D, int layout, int add,
+                                              int rms, hipStream_t stream) {
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  const FwdEpi ep{layout, add, rms};
+  if (D == 128) launch_f32<128, kGateVariant>(Q, K, V, G, Y, nullptr, B, 1, L, Hq, Hkv, scale_log2, stream, ep);
+  else launch_f32<64, kGateVariant>(Q, K, V, G, Y, nullptr, B, 1, L, Hq, Hkv, scale_log2, stream, ep);
+  return hipGetLastError();
+}
+
 }  // namespace gsa

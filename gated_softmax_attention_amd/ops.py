@@ -204,6 +204,35 @@ def forward_variant(Q, K, V, G, layout, combine="mul", norm=None, Y=None, LSE=No
     return Y if LSE is None else (Y, LSE)
 
 
+def decode_variant(Q, Kc, Vc, G, layout, combine="mul", norm=None, num_splits=0, Y=None, workspace=None,
+                   stream=None):
+    """One decode step with a design-space gate at the merge: combine(norm(Y), G)
+    with G [B, N] already activated, layout in LAYOUTS, combine "mul" or "add",
+    norm None or "rms"; other arguments as decode."""
+    B, one, Hq, D = Q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per batch")
+    L, Hkv = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
+    if layout not in LAYOUTS or combine not in ("mul", "add") or norm not in (None, "rms"):
+        raise ValueError("layout, combine or norm not recognised")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    need = decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits) if Q.dtype == torch.bfloat16 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gsa_decode_variant(
+        _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), None if G is None else _dev(G, "G"), _dev(Y, "Y"),
+        B, L, Hq, Hkv, D, LAYOUTS[layout], _lib.GSA_COMBINE_ADD if combine == "add" else _lib.GSA_COMBINE_MUL,
+        _lib.GSA_NORM_RMS if norm == "rms" else _lib.GSA_NORM_NONE, _dtype(Q, Kc, Vc, Y), num_splits, wp, wbytes,
+        _stream(stream)))
+    return Y
+
+
 def value_gate(V, G, layout, Vout=None, stream=None):
     """G2: V ⊙ G per key/value head (elementwise G [B*S, Hkv*D]) or per head
     (headwise G [B*S, Hkv]); returns the gated values, V's shape and dtype."""

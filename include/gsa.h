@@ -68,7 +68,7 @@ typedef enum gsa_activation {
   GSA_ACT_SILU = 3           /* Z·σ(Z) */
 } gsa_activation;
 
-/* How gsa_forward_variant applies the gate ("GatedAttention [2025]" §1.2.2 item (4)). */
+/* How gsa_forward_variant and gsa_decode_variant apply the gate ("GatedAttention [2025]" §1.2.2 item (4)). */
 typedef enum gsa_combine { GSA_COMBINE_MUL = 0, GSA_COMBINE_ADD = 1 } gsa_combine;
 
 /* Optional per-head normalisation of the SDPA output before the gate
@@ -213,6 +213,20 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
 gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, const float* G, void* Y,
                                float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                int layout, int combine, int norm, int dtype, void* stream);
+
+/*
+ * gsa_decode with the design-space epilogue of gsa_forward_variant, applied at
+ * the merge of the split partial results:
+ *   Y'[b,0,h,:] = combine(norm(Y[b,0,h,:]), gate)
+ * with Y gsa_decode's ungated output (one query per batch against all L
+ * cached keys).  layout, combine and norm as gsa_forward_variant, with the gate
+ * rows being the B decode tokens: G [B, Hq*D], [B, Hq] or [B, D] (already
+ * activated), NULL for GSA_GATE_NONE.  The workspace, num_splits and every
+ * other argument and rule as gsa_decode (the float32 path needs no workspace).
+ */
+gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
+                              int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int layout, int combine, int norm,
+                              int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * G2 value gating ("GatedAttention [2025]" §1.2.2, position G2): the gate

@@ -207,6 +207,35 @@ def test_forward_variant_argument_checks(lib):
     assert lib.gsa_last_error_message().decode().startswith("gsa_forward_variant")
 
 
+def test_decode_variant_argument_checks(lib):
+    need = lib.gsa_decode_workspace_bytes(2, 64, 4, 2, 128, 0)
+
+    def dv(Q=FAKE, G=FAKE, Y=FAKE, B=2, L=64, Hq=4, Hkv=2, D=128, layout=3, comb=1, norm=1, dtype=1, ns=0,
+           ws=FAKE, wsb=None):
+        return lib.gsa_decode_variant(Q, FAKE, FAKE, G, Y, B, L, Hq, Hkv, D, layout, comb, norm, dtype, ns, ws,
+                                      need if wsb is None else wsb, None)
+    assert dv(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(layout=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(comb=7) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(norm=2) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(G=None) == _lib.GSA_ERR_INVALID_ARG           # a gate layout needs G
+    assert dv(layout=0) == _lib.GSA_ERR_INVALID_ARG         # no gate but G given
+    assert dv(L=0) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(ns=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert dv(D=32) == _lib.GSA_ERR_UNSUPPORTED
+    assert dv(dtype=5) == _lib.GSA_ERR_UNSUPPORTED
+    assert dv(wsb=need - 1) == _lib.GSA_ERR_WORKSPACE      # bf16 needs the split workspace
+    assert dv(ws=None) == _lib.GSA_ERR_WORKSPACE
+    assert dv(Y=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert dv(ws=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert lib.gsa_last_error_message().decode().startswith("gsa_decode_variant")
+    # float32 takes no workspace: with valid arguments only the device check
+    # remains (asked only where no GPU is visible, so the fake pointers are never launched)
+    if not have_gpu():
+        assert dv(dtype=0, ws=None, wsb=0) == _lib.GSA_ERR_NO_DEVICE
+
+
 def test_value_gate_argument_checks(lib):
     def vg(V=FAKE, G=FAKE, Vo=FAKE, B=1, S=8, Hkv=2, D=128, layout=1, dtype=1):
         return lib.gsa_value_gate(V, G, Vo, B, S, Hkv, D, layout, dtype, None)

@@ -11,7 +11,7 @@ import oracle
 from oracle import variants as ov
 import gated_softmax_attention_amd as gsa
 from synth import CONFIGS, make_inputs
-from helpers import TOL, f64, report, sample_rows
+from helpers import TOL, f64, report, sample_rows, guarded_empty, guard_ok
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -115,3 +115,52 @@ def test_forward_variant_dense_prefill_sampled(layout, combine, norm):
     got, want, act = run_variant(cfg, layout, combine, norm, seed=0, rows=rows)
     report(got, want, TOL["bf16"] * max(1.0, float(np.abs(want).max()) / 4),
            f"dense_prefill {layout}/{combine}/{norm}/{act} sampled rows")
+
+
+def run_decode_variant(B, L, Hq, Hkv, D, dtype, layout, combine, norm, seed, num_splits=0):
+    cfg = CONFIGS["decode"].with_(name="d", B=B, L=L, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, d_model=64, mode="none")
+    inp = make_inputs(cfg, seed=seed, device=DEV)
+    N = gate_width(layout, Hq, D)
+    act = ACT_FOR.get((combine, layout), "sigmoid")
+    G = W = None
+    if N:
+        gx = torch.Generator(device=DEV).manual_seed(seed + 5)
+        W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
+        G = gsa.gate_logits(inp["X"].reshape(B, cfg.d_model), W, activation=act)
+    Y, guard = guarded_empty(tuple(inp["Q"].shape), inp["Q"].dtype, DEV)
+    gsa.decode_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm, num_splits=num_splits, Y=Y)
+    torch.cuda.synchronize()
+    assert guard_ok(guard), "write past the end of Y"
+    want = ov.gated_sdpa_variant(f64(inp["X"]), None if W is None else f64(W), f64(inp["Q"]), f64(inp["K"]),
+                                 f64(inp["V"]), layout, act, combine, norm)
+    return f64(Y), want, act
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("layout,combine,norm", CASES)
+def test_decode_variant_small(layout, combine, norm, dtype):
+    for (B, L, Hq, Hkv, D) in [(3, 777, 8, 2, 128), (2, 65, 4, 4, 64), (1, 1, 4, 1, 128)]:
+        got, want, act = run_decode_variant(B, L, Hq, Hkv, D, dtype, layout, combine, norm, seed=L + Hq)
+        tol = TOL[dtype] * max(1.0, float(np.abs(want).max()) / 4)
+        report(got, want, tol, f"decode {dtype} {layout}/{combine}/{norm}/{act} B{B} L{L} {Hq}/{Hkv} D{D}")
+
+
+@pytest.mark.parametrize("ns", [1, 3, 16])
+def test_decode_variant_split_counts(ns):
+    # the RMS norm is taken after the split partials are merged: any split
+    # count gives the same head-wide normaliser
+    got, want, act = run_decode_variant(2, 2049, 8, 2, 128, "bf16", "shared", "add", "rms", seed=21, num_splits=ns)
+    report(got, want, TOL["bf16"] * max(1.0, float(np.abs(want).max()) / 4), f"decode variant splits {ns}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mode", ["elementwise", "headwise", "none"])
+def test_default_decode_variant_equals_decode_bitwise(mode, dtype):
+    cfg = CONFIGS["decode"].with_(name="d", B=3, L=1500, Hq=16, Hkv=4, D=128, dtype=dtype, d_model=64, mode=mode)
+    inp = make_inputs(cfg, seed=4, device=DEV)
+    G = None if mode == "none" else gsa.gate_logits(inp["X"], inp["W"])
+    a = gsa.decode(inp["Q"], inp["K"], inp["V"], G, mode)
+    b = gsa.decode_variant(inp["Q"], inp["K"], inp["V"], G, mode, "mul", None)
+    torch.cuda.synchronize()
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(a.view(itype), b.view(itype))
