@@ -417,6 +417,118 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if (it + 1 < n_kv) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
   }
 
+  if constexpr (QB == 1) {
+    // Epilogue through LDS.  In the accumulator layout a lane holds one row and
+    // 16-byte pieces of it 32 bytes apart, so a store (or gate load) there
+    // touches 32 rows at once; staged through LDS, each instruction covers
+    // whole rows instead (two at D = 128, four at D = 64), with 4-8x fewer
+    // cache lines per instruction.  The loop's last barrier came after every
+    // wave's last LDS read and direct load, so the stage arrays are free: wave
+    // w stages its 32 rows of float32 in the w-th of them (32·D·4 bytes, the
+    // size of a V stage), chunk c of row r in slot c ^ (r & 15), so that both
+    // the accumulator-layout writes (16 rows per 16 lanes) and the row reads
+    // (16 chunks of one row per 16 lanes) fall on distinct banks.  The value
+    // stored is still round((o · (1/l)) · g), as in the register epilogue (for
+    // the design-space variants round(combine(o · (1/l) · rn, g))).
+    const float l_tot = l_run[0] + __shfl_xor(l_run[0], 32);  // the two halves summed different keys
+    const bool row_ok = my_q[0] < S;
+    if (Lse != nullptr && hl == 0 && row_ok)
+      Lse[((int64_t)b * Hq + head) * S + my_q[0]] = (m_run[0] + log2f(l_tot)) * kLn2;
+    const float inv = 1.0f / l_tot;
+    float rn = 1.0f;   // the variants' RMSNorm factor of the row
+    if constexpr (MODE == kGateVariant) {
+      if (ep.rms) {
+        // the row's D values sit in this lane (half) and in lane ^ 32 (other half)
+        float ss = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = o[0][dt][r] * inv;
+            ss = fmaf(y, y, ss);
+          }
+        ss += __shfl_xor(ss, 32);
+        rn = 1.0f / sqrtf(ss / (float)D + kRmsEps);
+      }
+    }
+    constexpr int LPR = D / 4;       // lanes per row in the row pattern (16 bytes each)
+    constexpr int RPI = 64 / LPR;    // rows per instruction
+    constexpr int NI = 32 / RPI;     // instructions for the wave's 32 rows
+    const int sr = lane / LPR, sc = lane % LPR;
+    // elementwise gate: the coalesced row loads go first, before any store
+    // (the memory counter the waits use also counts stores); rows past the end
+    // read the last row instead and are not stored
+    f32x4 gv[NI];
+    if constexpr (MODE == kGateElem) {
+      const float* const grow = Gate + (int64_t)head * D + 4 * sc;
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int q = min(qw0 + RPI * n + sr, S - 1);
+        gv[n] = *(const f32x4*)(grow + ((int64_t)b * S + q) * q_row);
+      }
+#pragma unroll
+      for (int n = 0; n < NI; ++n) asm volatile("" : "+v"(gv[n]));
+    }
+    if constexpr (MODE == kGateVariant) {
+      if (ep.layout != kGateNone) {
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+          const int64_t tok = (int64_t)b * S + min(qw0 + RPI * n + sr, S - 1);
+          if (ep.layout == kGateHead) {
+            const float g = Gate[tok * Hq + head];
+            gv[n] = f32x4{g, g, g, g};
+          } else {
+            gv[n] = *(const f32x4*)(Gate + (ep.layout == kGateElem ? (tok * Hq + head) * D : tok * D) + 4 * sc);
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < NI; ++n) asm volatile("" : "+v"(gv[n]));
+      }
+    }
+    float gh = 1.0f;
+    if constexpr (MODE == kGateHead) gh = Gate[((int64_t)b * S + min(my_q[0], S - 1)) * Hq + head];
+    GSA_LDS char* const stg = wave == 0   ? (GSA_LDS char*)(GSA_LDS void*)Ks0
+                              : wave == 1 ? (GSA_LDS char*)(GSA_LDS void*)Ks1
+                              : wave == 2 ? (GSA_LDS char*)(GSA_LDS void*)Vs0
+                                          : (GSA_LDS char*)(GSA_LDS void*)Vs1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 8 * dt + 2 * i + hl;   // 16-byte chunk of dims dt*32 + 8i + 4hl .. +3
+        f32x4 t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (MODE == kGateVariant) t[j] = o[0][dt][4 * i + j] * inv * rn;
+          else t[j] = o[0][dt][4 * i + j] * inv;
+          if constexpr (MODE == kGateHead) t[j] *= gh;
+        }
+        *(GSA_LDS f32x4*)(stg + l32 * (4 * D) + ((c ^ (l32 & 15)) * 16)) = t;
+      }
+    // the rows are read back by other lanes of this wave: its LDS writes must
+    // have completed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int r = RPI * n + sr;
+      f32x4 t = *(GSA_LDS const f32x4*)(stg + r * (4 * D) + ((sc ^ (r & 15)) * 16));
+      if constexpr (MODE == kGateElem) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] *= gv[n][j];
+      }
+      if constexpr (MODE == kGateVariant) {
+        if (ep.layout != kGateNone) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) t[j] = variant_combine(t[j], gv[n][j], ep);
+        }
+      }
+      if (qw0 + r < S)
+        *(u32x2*)(Y + ((int64_t)b * S + qw0 + r) * q_row + (int64_t)head * D + 4 * sc) =
+            u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+    }
+    return;
+  }
+
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     // every lane takes part in the exchange; rows past the end store nothing
