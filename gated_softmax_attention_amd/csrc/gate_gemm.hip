@@ -484,7 +484,7 @@ void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __rest
     const int st = kt % NS;
     if (kt + NS - 1 < nk) {
       dma((kt0 + kt + NS - 1) * BK, (kt + NS - 1) % NS);
-      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // the 3 newer stages (8 loads each) may still fly
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(8 * (NS - 1)) : "memory");   // the NS-1 newer stages (8 loads each) may still fly
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
