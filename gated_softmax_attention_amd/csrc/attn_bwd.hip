@@ -290,12 +290,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const auto vrs = make_rsrc(V + (int64_t)b * S * kv_row + (int64_t)kvh * D, kv_bytes);
   TileLoader<D, KT> ld;
   ld.init(wave, lane, row_b);
-  uint32_t ks_lds[2], vs_lds[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    ks_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[i][0]));
-    vs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[i][0]));
-  }
+  const uint32_t ks_lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[0][0]));
+  const uint32_t vs_lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]));
   TrAddr trb[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) trb[dt] = tr_addr<D>(lane, dt);
@@ -308,15 +304,18 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
   const int kv_end = min(S, q0 + QT);
   const int n_kv = ceil_div(kv_end, KT);
-  ld.load(krs, row_b, 0, S, ks_lds[0], wave);
-  ld.load(vrs, row_b, 0, S, vs_lds[0], wave);
-  for (int it = 0; it < n_kv; ++it) {
-    const int buf = it & 1, k0 = it * KT;
+  ld.load(krs, row_b, 0, S, ks_lds0, wave);
+  ld.load(vrs, row_b, 0, S, vs_lds0, wave);
+  // one key tile with its stage known at compile time (the loop below is
+  // unrolled by two), so every LDS address is a constant offset from the base
+  auto one_tile = [&](auto stage, int it) {
+    constexpr int buf = decltype(stage)::value;
+    const int k0 = it * KT;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (it + 1 < n_kv) {
-      ld.load(krs, row_b, k0 + KT, S, ks_lds[buf ^ 1], wave);
-      ld.load(vrs, row_b, k0 + KT, S, vs_lds[buf ^ 1], wave);
+      ld.load(krs, row_b, k0 + KT, S, ks_lds0 + (buf ^ 1) * (KT * RSB), wave);
+      ld.load(vrs, row_b, k0 + KT, S, vs_lds0 + (buf ^ 1) * (KT * RSB), wave);
     }
     const GSA_LDS_B char* kt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ks[buf][0];
     const GSA_LDS_B char* vt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Vs[buf][0];
@@ -364,18 +363,42 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
         for (int dt = 0; dt < D / 32; ++dt)
           acc[dt] = mfma32x32x16(tr_read(kt + (sub * 32 + 16 * t) * RSB, trb[dt]), ds, acc[dt]);
       }
+  };
+  for (int it = 0; it < n_kv; it += 2) {
+    one_tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_kv) one_tile(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  if (my_q >= S) return;
-  bf16* out = dQ + ((int64_t)b * S + my_q) * q_row + (int64_t)head * D;
+  // Store through LDS: a lane holds one query row in 16-byte pieces 32 bytes
+  // apart, so a direct store would touch 32 rows at once.  Each wave stages
+  // its 32 rows of float32 dQ in one of the four tile buffers (free once every
+  // wave is past the loop), chunk c of row r in slot c ^ (r & 15) (distinct
+  // banks for both access patterns), and reads them back by rows.
+  static_assert(KT * RSB >= 32 * 4 * D, "a tile buffer holds one wave's 32 rows of float32");
+  __syncthreads();
+  char* const stg = wave == 0 ? &Ks[0][0] : wave == 1 ? &Ks[1][0] : wave == 2 ? &Vs[0][0] : &Vs[1][0];
+  GSA_LDS_B char* const sg = (GSA_LDS_B char*)(GSA_LDS_B void*)stg;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int d0 = dt * 32 + 8 * i + 4 * hl;
-      *(u32x2*)(out + d0) = u32x2{pack_bf16x2(acc[dt][4 * i] * scale, acc[dt][4 * i + 1] * scale),
-                                  pack_bf16x2(acc[dt][4 * i + 2] * scale, acc[dt][4 * i + 3] * scale)};
+      const int c = 8 * dt + 2 * i + hl;   // 16-byte chunk of dims dt*32 + 8i + 4hl .. +3
+      *(GSA_LDS_B f32x4*)(sg + l32 * (4 * D) + (c ^ (l32 & 15)) * 16) =
+          f32x4{acc[dt][4 * i] * scale, acc[dt][4 * i + 1] * scale, acc[dt][4 * i + 2] * scale,
+                acc[dt][4 * i + 3] * scale};
     }
+  // the rows are read back by other lanes of this wave
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int LPR = D / 4, RPI = 64 / LPR;
+  const int sr = lane / LPR, sc = lane % LPR;
+#pragma unroll
+  for (int n = 0; n < 32 / RPI; ++n) {
+    const int r = RPI * n + sr;
+    const f32x4 v = *(const GSA_LDS_B f32x4*)(sg + r * (4 * D) + (sc ^ (r & 15)) * 16);
+    if (qw0 + r < S)
+      *(u32x2*)(dQ + ((int64_t)b * S + qw0 + r) * q_row + (int64_t)head * D + 4 * sc) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -581,7 +604,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 //     B operand of dP (a 16-byte row read per k step) instead of living in
 //     registers;
 //   * query tiles are 32 rows, halving the S and dP accumulators.
-// K fragments and the dK/dV accumulators stay in registers.
+// K fragments and the dK/dV accumulators stay in registers.  Query tiles are
+// double-buffered: the next tile's loads fly while one is consumed.
 template <int D, bool PARTIAL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES)
 void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -634,13 +658,10 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const uint32_t row_b = (uint32_t)(q_row * 2);
   TileLoader<D, QR, WAVES> ld;
   ld.init(wave, lane, row_b);
-  uint32_t qs_lds[2], ys_lds[2], st_lds[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    qs_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Qs[i][0]));
-    ys_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ys[i][0]));
-    st_lds[i] = __builtin_amdgcn_readfirstlane(lds_addr(&Ss[i][0]));
-  }
+  // stage i of each array sits i whole stages past stage 0
+  const uint32_t qs_lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&Qs[0][0]));
+  const uint32_t ys_lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ys[0][0]));
+  const uint32_t st_lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ss[0][0]));
   // statistics loads (wave 0): lanes 0..7 take 4 LSE rows each, lanes 8..15 4 D rows
   const auto srs = make_rsrc(Stat, (uint32_t)((int64_t)2 * B * Hq * Sp * 4));
   const uint32_t st_lane = lane < 8 ? 16u * lane : (uint32_t)((int64_t)B * Hq * Sp * 4) + 16u * (lane - 8);
@@ -672,23 +693,26 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const uint32_t bytes = (uint32_t)(((int64_t)S * q_row - (int64_t)head * D) * 2);
     const auto qr = make_rsrc(Q + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
     const auto yr = make_rsrc(dY + (int64_t)b * S * q_row + (int64_t)head * D, bytes);
-    ld.load(qr, row_b, qs0, S, qs_lds[buf], wave);
-    ld.load(yr, row_b, qs0, S, ys_lds[buf], wave);
+    ld.load(qr, row_b, qs0, S, qs_lds0 + (uint32_t)buf * QB, wave);
+    ld.load(yr, row_b, qs0, S, ys_lds0 + (uint32_t)buf * QB, wave);
     if (wave == 0)
       dma16_lds(srs, lane < 16 ? st_lane + (uint32_t)(((int64_t)b * Hq + head) * Sp + qs0) * 4u : kOOB,
-                st_lds[buf]);
+                st_lds0 + (uint32_t)buf * 1024u);
   };
   const GSA_LDS_B char* vt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Vt[0];
   if (n_steps > 0) issue(0, 0);
-  for (int step = 0; step < n_steps; ++step) {
-    const int buf = step & 1;
+  // one step with its stage known at compile time (the loop below is unrolled
+  // by two), so every LDS address is a constant offset from the stage base
+  auto one_step = [&](auto stage, int step) {
+    constexpr int buf = decltype(stage)::value;
     int head, qs0;
     tile_of(step, head, qs0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // the stage refilled here was consumed in step - 1, before the barrier
     if (step + 1 < n_steps) issue(step + 1, buf ^ 1);
     // a wave whose keys all come after the tile's last query gets P = dS = 0
-    if (kw0 > qs0 + QR - 1) continue;
+    if (kw0 > qs0 + QR - 1) return;
     const GSA_LDS_B char* qt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Qs[buf][0];
     const GSA_LDS_B char* yt = (const GSA_LDS_B char*)(GSA_LDS_B void*)&Ys[buf][0];
     const GSA_LDS_B float* st = (const GSA_LDS_B float*)(GSA_LDS_B void*)&Ss[buf][0];
@@ -740,6 +764,10 @@ void bwd_dkdv_vlds_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
         dk[dt] = mfma32x32x16(tr_read(qt + ro, trb[dt]), db, dk[dt]);
       }
     }
+  };
+  for (int step = 0; step < n_steps; step += 2) {
+    one_step(std::integral_constant<int, 0>{}, step);
+    if (step + 1 < n_steps) one_step(std::integral_constant<int, 1>{}, step + 1);
   }
 
   if (my_k >= S) return;
