@@ -164,3 +164,25 @@ def test_default_decode_variant_equals_decode_bitwise(mode, dtype):
     torch.cuda.synchronize()
     itype = torch.int16 if dtype == "bf16" else torch.int32
     assert torch.equal(a.view(itype), b.view(itype))
+
+
+@pytest.mark.parametrize("layout,combine,norm", [("shared", "add", "rms"), ("headwise", "mul", None)])
+def test_decode_variant_full_size_sampled(layout, combine, norm):
+    """The decode workload (B 64, L 16384, 32/8 heads) in the launch bench.py
+    times, checked on sampled batches against the oracle."""
+    cfg = CONFIGS["decode"].with_(mode="none")
+    print("  decode variant: generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=2, device=DEV)
+    N = gate_width(layout, cfg.Hq, cfg.D)
+    act = ACT_FOR[(combine, layout)]
+    gx = torch.Generator(device=DEV).manual_seed(7)
+    W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
+    G = gsa.gate_logits(inp["X"].reshape(cfg.B, cfg.d_model), W, activation=act)
+    Y = gsa.decode_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y.float()).any()
+    bs = [0, 31, 63]
+    want = ov.gated_sdpa_variant(f64(inp["X"][bs]), f64(W), f64(inp["Q"][bs]), f64(inp["K"][bs]),
+                                 f64(inp["V"][bs]), layout, act, combine, norm)
+    report(f64(Y[bs]), want, TOL["bf16"] * max(1.0, float(np.abs(want).max()) / 4),
+           f"decode full size {layout}/{combine}/{norm}, batches {bs}")
