@@ -326,3 +326,10 @@ def test_error_messages_are_per_thread(lib):
         t.join()
     for i, msgs in results.items():
         assert all(st == _lib.GSA_ERR_UNSUPPORTED and ok for st, ok in msgs), i
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # the binding has no fallback path: without libgsa.so every call raises
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        _lib.load(str(tmp_path / "libgsa.so"))
