@@ -396,6 +396,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, torch)
         return
+    from gated_softmax_attention_amd.build import ensure_built
+    ensure_built()   # load what is built; build only when nothing is
     import gated_softmax_attention_amd as gsa
     from synth import CONFIGS
     gsa.load_library()

@@ -49,5 +49,14 @@ def build(verbose: bool = False, out: str = LIB_PATH, csrc: str = CSRC, extra=()
     return out
 
 
+def ensure_built(verbose: bool = False) -> str:
+    """The tests, the smoke check and the bench load the library that is built;
+    only when none is there do they build it first.  (The binding itself never
+    builds: without libgsa.so it raises.)"""
+    if not os.path.exists(LIB_PATH):
+        build(verbose=verbose)
+    return LIB_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -10,6 +10,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # load what is built; build only when nothing is
+    from gated_softmax_attention_amd.build import ensure_built
+    ensure_built(verbose=True)
 
 
 def pytest_collection_modifyitems(config, items):
