@@ -56,7 +56,7 @@ typedef enum gsa_gate_mode {
   GSA_GATE_ELEMENTWISE = 1,  /* G is [rows, Hq*D]; column h*D + d gates head h, dim d */
   GSA_GATE_HEADWISE = 2,     /* G is [rows, Hq];   column h gates all of head h       */
   GSA_GATE_SHARED = 3        /* G is [rows, D];    column d gates dim d of every head
-                                (gsa_forward_variant only) */
+                                (gsa_forward_variant and gsa_decode_variant only) */
 } gsa_gate_mode;
 
 /* Gate activation applied by gsa_gate_logits ("GatedAttention [2025]" §1.2.2
@@ -215,7 +215,8 @@ gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, cons
                                int layout, int combine, int norm, int dtype, void* stream);
 
 /*
- * gsa_decode with the design-space epilogue of gsa_forward_variant, applied at
+ * gsa_decode with the design-space epilogue of gsa_forward_variant ("GatedAttention
+ * [2025]" §1.2.2 items (3)-(5) and §1.4.1, on the KV cache of §1.3.1), applied at
  * the merge of the split partial results:
  *   Y'[b,0,h,:] = combine(norm(Y[b,0,h,:]), gate)
  * with Y gsa_decode's ungated output (one query per batch against all L
@@ -223,6 +224,8 @@ gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, cons
  * rows being the B decode tokens: G [B, Hq*D], [B, Hq] or [B, D] (already
  * activated), NULL for GSA_GATE_NONE.  The workspace, num_splits and every
  * other argument and rule as gsa_decode (the float32 path needs no workspace).
+ * Errors: an unknown layout, combine or norm, or G given with GSA_GATE_NONE (or
+ * missing with a gate) -> GSA_ERR_INVALID_ARG; the rest as gsa_decode.
  */
 gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
                               int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int layout, int combine, int norm,
