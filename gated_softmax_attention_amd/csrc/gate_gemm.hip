@@ -417,14 +417,24 @@ constexpr uint32_t kOOB = 0xfffffff0u;
 __global__ __launch_bounds__(256)
 void gate_gemm_bf16_narrow_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
                                   float* __restrict__ G, int M, int K, int N, int tiles_n,
-                                  int act) {
+                                  int act, int w_major) {
   using namespace gemm_narrow;
   __shared__ __align__(16) bf16 Xs[WAVES][NS][XSLOTS * 8];
   __shared__ __align__(16) bf16 Ws[WAVES][NS][WSLOTS * 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  // Tile order: workgroup ids go round-robin over the 8 XCDs, and XCD x takes
+  // the x-th contiguous eighth of the tile list (when the count allows), so
+  // tiles next to each other in the list share an L2.  With w_major the list
+  // runs over row tiles first (tiles of one column block, which read the same
+  // W_θ columns, are adjacent: for few rows W_θ is the large operand); else
+  // over column tiles first (tiles of one row block share their X rows).
+  const int tiles = (int)gridDim.x, bid = blockIdx.x;
+  const int t = tiles % 8 == 0 ? (bid % 8) * (tiles / 8) + bid / 8 : bid;
+  const int tiles_m = tiles / tiles_n;
+  const int tm = w_major ? t % tiles_m : t / tiles_n;
+  const int tn = w_major ? t / tiles_m : t % tiles_n;
   const int m0 = tm * 32, n0 = tn * 32;
 
   // this wave's k range: a whole number of BK steps
@@ -581,9 +591,11 @@ hipError_t launch_gate_gemm(const void* X, const void* W, float* G, int64_t M, i
   } else if (bf16_inputs && N % 8 == 0 && M * K * 2 < (int64_t(1) << 31) && K * N * 2 < (int64_t(1) << 31)) {
     const int tiles_n = (int)ceil_div<int64_t>(N, 32);
     const int64_t tiles = ceil_div<int64_t>(M, 32) * tiles_n;
+    // the larger operand is shared within an XCD: W_θ (K·N) when it exceeds X (M·K)
+    const int w_major = N > M ? 1 : 0;
     hipLaunchKernelGGL(gate_gemm_bf16_narrow_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        (const bf16*)X, (const bf16*)W, G, (int)M, (int)K, (int)N, tiles_n,
-                       act);
+                       act, w_major);
   } else if (bf16_inputs) {
     const int tiles_n = (int)ceil_div<int64_t>(N, gemm::BN);
     const int64_t tiles = ceil_div<int64_t>(M, gemm::BM) * tiles_n;
