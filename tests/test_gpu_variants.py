@@ -108,13 +108,18 @@ def test_value_gating_g2(layout, dtype):
     report(f64(Y), want, TOL[dtype], f"G2 {dtype} {layout}")
 
 
-@pytest.mark.parametrize("layout,combine,norm", [("shared", "add", "rms"), ("headwise", "mul", "rms")])
-def test_forward_variant_dense_prefill_sampled(layout, combine, norm):
-    cfg = CONFIGS["dense_prefill"]
+@pytest.mark.parametrize("name,layout,combine,norm", [("dense_prefill", "shared", "add", "rms"),
+                                                     ("dense_prefill", "headwise", "mul", "rms"),
+                                                     ("gqa_prefill", "shared", "add", "rms"),
+                                                     ("gqa_prefill", "elementwise", "add", None)])
+def test_forward_variant_full_size_sampled(name, layout, combine, norm):
+    """Full-size prefill workloads (gqa_prefill: S 8192, 32/4 heads, d_model
+    4096) through the design-space epilogue, checked on sampled rows."""
+    cfg = CONFIGS[name]
     rows = sample_rows(cfg.S)
     got, want, act = run_variant(cfg, layout, combine, norm, seed=0, rows=rows)
     report(got, want, TOL["bf16"] * max(1.0, float(np.abs(want).max()) / 4),
-           f"dense_prefill {layout}/{combine}/{norm}/{act} sampled rows")
+           f"{name} {layout}/{combine}/{norm}/{act} sampled rows")
 
 
 def run_decode_variant(B, L, Hq, Hkv, D, dtype, layout, combine, norm, seed, num_splits=0):
