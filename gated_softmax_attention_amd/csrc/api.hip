@@ -266,6 +266,82 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
                     "gsa_decode launch");
 }
 
+}  // extern "C"
+
+namespace {
+// Device-resident scratch for gsa_decode_noalloc: the split partials that
+// gsa_decode keeps in the caller's workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses the
+// array's name as an address: its device address is looked up once per device
+// and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)GSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device, with it current); nullptr and the HIP error on failure.
+void* scratch_address(int dev, hipError_t* err) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = p;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t gsa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
+                              int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype, int num_splits,
+                              void* stream) {
+  const char* fn = "gsa_decode_noalloc";
+  if (!Q || !Kc || !Vc || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (gsa_status st = check_attn_shape(fn, B, L, Hq, Hkv, D, mode, G, 1)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
+    return fail(GSA_ERR_MISALIGNED, "%s: Q, Kc, Vc, G and Y must be 16-byte aligned", fn);
+  int64_t ns = 0;
+  if (dtype == GSA_BF16) {
+    ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+    const size_t need = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
+    if (need > kNoAllocScratchBytes)
+      return fail(GSA_ERR_WORKSPACE,
+                  "%s: these sizes need %zu bytes of split partials, more than the %zu-byte device scratch "
+                  "(fewer splits or a smaller batch fit; gsa_decode takes a caller workspace of any size)",
+                  fn, need, kNoAllocScratchBytes);
+  }
+  if (gsa_status st = check_device()) return st;
+  if (dtype != GSA_BF16)  // float32 decode needs no scratch
+    return hip_result(gsa::launch_attn_fwd(Q, Kc, Vc, G, Y, nullptr, (int)B, 1, (int)L, (int)Hq, (int)Hkv, (int)D,
+                                           mode, false, (hipStream_t)stream),
+                      fn);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GSA_ERR_NO_DEVICE, "%s: hipGetDevice failed", fn);
+  }
+  hipError_t e = hipSuccess;
+  void* ws = scratch_address(dev, &e);
+  if (ws == nullptr) return fail(GSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+  return hip_result(gsa::launch_decode_bf16(Q, Kc, Vc, G, Y, ws, (int)B, (int)L, (int)Hq, (int)Hkv, (int)D, mode,
+                                            (int)ns, (hipStream_t)stream),
+                    fn);
+}
+
 gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
                               int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int layout, int combine, int norm,
                               int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {

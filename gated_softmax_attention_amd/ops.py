@@ -138,6 +138,31 @@ def decode(Q, Kc, Vc, G, mode, num_splits=0, Y=None, workspace=None, stream=None
     return Y
 
 
+def noalloc_scratch_bytes():
+    return int(_lib.load().gsa_noalloc_scratch_bytes())
+
+
+def decode_noalloc(Q, Kc, Vc, G, mode, Y, num_splits=0, stream=None):
+    """decode() through gsa_decode_noalloc: the split partials live in the
+    library's own device scratch, and nothing is allocated here either, so the
+    caller passes the output Y [B,1,Hq,D].  Calls that overlap in time on one GPU
+    race on that scratch."""
+    B, one, Hq, D = Q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per batch")
+    L, Hkv = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
+    if Y is None or Y.shape != Q.shape:
+        raise ValueError("Y must be given, with Q's shape")
+    gp = None if G is None else _dev(G, "G")
+    lib = _lib.load()
+    _lib.check(lib.gsa_decode_noalloc(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), gp, _dev(Y, "Y"),
+                                      B, L, Hq, Hkv, D, _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits,
+                                      _stream(stream)))
+    return Y
+
+
 def backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, mode):
     return int(_lib.load().gsa_backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, _mode(mode)))
 

@@ -16,7 +16,8 @@
  * Conventions for every entry point:
  *  - Pointers X, W, G, Q, K, V, Y, workspace are DEVICE pointers owned by the
  *    caller, to contiguous row-major tensors, each 16-byte aligned.  The library
- *    allocates nothing and keeps no per-call state.
+ *    allocates nothing and keeps no per-call state (gsa_decode_noalloc keeps its
+ *    split partials in a fixed device array inside the library).
  *  - dtype (gsa_dtype) is the element type of X, W, Q, K, V and Y'.  G is always
  *    float32.  Arithmetic is float32 (bf16 inputs multiply exactly into float32
  *    accumulators on the matrix cores).
@@ -27,7 +28,8 @@
  *    a host without a GPU (which then gets GSA_ERR_NO_DEVICE).  A per-thread
  *    message describing the last failure is available from
  *    gsa_last_error_message().
- *  - Calls are thread-safe; concurrent calls on different streams are allowed.
+ *  - Calls are thread-safe; concurrent calls on different streams are allowed
+ *    (except gsa_decode_noalloc, whose calls on one GPU share a device scratch).
  */
 #ifndef GSA_H
 #define GSA_H
@@ -155,6 +157,35 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
                       int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
                       int mode, int dtype, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device scratch gsa_decode_noalloc uses for its split partials:
+   8 MiB per GPU, enough for B·Hq·nsplit·(D+4) float32 values up to 2097152
+   (e.g. 64 batches × 32 query heads × 7 splits at D = 128). */
+#define GSA_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* GSA_NOALLOC_SCRATCH_BYTES, as the library was built with it. */
+size_t gsa_noalloc_scratch_bytes(void);
+
+/*
+ * gsa_decode for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace and allocates nothing (no hipMalloc, hipFree or allocating library
+ * call).  The split partials go to a device array inside the library, one per
+ * GPU, of GSA_NOALLOC_SCRATCH_BYTES; each GPU holds it until the process ends.
+ * Same arguments, results and kernels as gsa_decode without the workspace
+ * pair; the caller still allocates Q, Kc, Vc, G and Y.
+ * Errors: as gsa_decode; sizes whose partials
+ * (gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits)) exceed
+ * GSA_NOALLOC_SCRATCH_BYTES -> GSA_ERR_WORKSPACE (use fewer splits, or
+ * gsa_decode).  float32 decode needs no scratch.
+ * Concurrency: every call on one GPU shares that GPU's scratch and leaves its
+ * partials there; two calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and may return wrong results.
+ * Calls ordered on one stream are safe.
+ */
+gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y,
+                              int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                              int mode, int dtype, int num_splits, void* stream);
 
 /*
  * Workspace bytes gsa_backward needs for these sizes (0 for invalid sizes;

@@ -70,3 +70,16 @@ def sample_rows(S, extra_random=4, seed=0):
     rng = np.random.default_rng(seed)
     base += [int(x) for x in rng.integers(0, S, size=extra_random)]
     return sorted({r for r in base if 0 <= r < S})
+
+
+def oracle_decode_by_batch(inp, mode, batches=None):
+    """Oracle decode output [B', 1, Hq, D] for every batch (or the listed ones),
+    one batch at a time so the fp64 copy of the cache stays one batch's size."""
+    X, W, Q, K, V = (inp[k] for k in "XWQKV")
+    bl = range(Q.shape[0]) if batches is None else batches
+    Wf = f64(W) if W is not None else None
+    out = []
+    for b in bl:
+        out.append(oracle.gated_decode(f64(X[b:b + 1]), Wf, f64(Q[b:b + 1]), f64(K[b:b + 1]),
+                                       f64(V[b:b + 1]), mode)[0])
+    return np.stack(out)

@@ -108,6 +108,27 @@ def test_decode_argument_checks(lib):
     assert dec(ws=MIS) == _lib.GSA_ERR_MISALIGNED
 
 
+def test_decode_noalloc_argument_checks(lib):
+    def dec(Q=FAKE, G=FAKE, B=2, L=100, Hq=8, Hkv=2, D=128, mode=1, dtype=1, ns=0):
+        return lib.gsa_decode_noalloc(Q, FAKE, FAKE, G, FAKE, B, L, Hq, Hkv, D, mode, dtype, ns, None)
+    assert lib.gsa_noalloc_scratch_bytes() == 8 << 20
+    assert dec(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(L=0) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(ns=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(G=None) == _lib.GSA_ERR_INVALID_ARG
+    assert dec(D=32) == _lib.GSA_ERR_UNSUPPORTED
+    assert dec(Q=MIS) == _lib.GSA_ERR_MISALIGNED
+    # partials beyond the 8 MiB device scratch are refused before any device call:
+    # 64 x 32 heads x 7 splits x 132 floats fit, 8 splits do not
+    assert lib.gsa_decode_workspace_bytes(64, 16384, 32, 8, 128, 7) <= 8 << 20
+    assert dec(B=64, L=16384, Hq=32, Hkv=8, ns=8) == _lib.GSA_ERR_WORKSPACE
+    assert b"scratch" in lib.gsa_last_error_message()
+    if not have_gpu():
+        assert dec(B=64, L=16384, Hq=32, Hkv=8, ns=7) == _lib.GSA_ERR_NO_DEVICE
+        assert dec(dtype=0, B=64, L=16384, Hq=32, Hkv=8, ns=64) == _lib.GSA_ERR_NO_DEVICE  # fp32: no scratch
+
+
 def test_size_limits(lib):
     # one batch of Q (prefill) above 2 GiB at the float32 size
     assert fwd(lib, S=1 << 20, Hq=8, Hkv=8, D=128) == _lib.GSA_ERR_UNSUPPORTED
