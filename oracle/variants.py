@@ -3,9 +3,14 @@
 The "GatedAttention [2025]" page's §1.2.2 lays out the axes a gate can vary
 along, with G1 (SDPA output) as the main position:
 
-  * head-specific or head-shared scores (item (3)): head-shared uses one gate
-    vector of width d_k per token for every query head (the Table 1 discussion
-    averages the n×q×d_k score over the q heads to get n×d_k);
+  * head-specific or head-shared scores (item (3)): head-shared gives every
+    query head the same gating score of width d_k per token.  The §1.3.2
+    Table 1 discussion (observation (ii)) says how it is formed: the n×q×d_k
+    gating scores are averaged over the q query heads into an n×d_k score.
+    The gating score is the activated value act(X·W_θ) (the quantity §1.2.2
+    calls the score and multiplies into Y), so the average is taken after the
+    activation, and W_θ keeps the elementwise width q·d_k ("10 · 门控" §3.2,
+    Table 1 row 12 prices head-shared at 201 M, the same as row 5);
   * multiplicative, Y' = Y ⊙ act(X·W_θ), or additive, Y' = Y + act(X·W_θ)
     (item (4));
   * the activation (item (5)): sigmoid (for multiplicative), SiLU(x) = x·σ(x)
@@ -44,21 +49,30 @@ def activation(Z, act):
     raise ValueError(act)
 
 
+def gate_width(mode, Hq, D):
+    """Columns of W_θ (per layer: d_model × gate_width parameters) each layout
+    consumes: q·d_k for elementwise and for head-shared (whose n×q×d_k scores
+    are then averaged over the q heads), q for headwise."""
+    if mode in ("elementwise", "shared"):
+        return Hq * D
+    if mode == "headwise":
+        return Hq
+    raise ValueError(mode)
+
+
 def gate_layout(a, Hq, D, mode):
     """Activated scores [B, S, N] arranged to broadcast against Y [B, S, Hq, D]:
     elementwise N = Hq·D -> [B, S, Hq, D]; headwise N = Hq -> [B, S, Hq, 1];
-    shared N = D -> [B, S, 1, D] (the same vector for every head)."""
+    shared N = Hq·D -> [B, S, 1, D], the mean over the Hq heads of the
+    elementwise arrangement (one vector for every head)."""
     B, S, N = a.shape
+    assert N == gate_width(mode, Hq, D)
     if mode == "elementwise":
-        assert N == Hq * D
         return a.reshape(B, S, Hq, D)
     if mode == "headwise":
-        assert N == Hq
         return a.reshape(B, S, Hq, 1)
-    if mode == "shared":
-        assert N == D
-        return a.reshape(B, S, 1, D)
-    raise ValueError(mode)
+    # shared: mean over the query-head axis of the [.., q, d_k] scores
+    return a.reshape(B, S, Hq, D).sum(axis=2, keepdims=True) / Hq
 
 
 def rms_norm_heads(Y, eps=RMS_EPS):

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import variants
 from oracle import brute
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -260,8 +261,15 @@ def test_gate_param_counts_match_table1():
         9: Lyr * dm * dm,
         10: Lyr * oracle.gate_param_count(dm, q, dk, "headwise"),
         11: Lyr * dm * k,
-        12: Lyr * oracle.gate_param_count(dm, q, dk, "elementwise"),
+        # head-shared: the width the variants oracle's layout consumes (the n×q×d_k
+        # scores it then averages over the q heads)
+        12: Lyr * dm * variants.gate_width("shared", q, dk),
     }
+    # that layout turns a score row of this width into one n×d_k gate for all heads
+    assert variants.gate_layout(np.zeros((1, 1, variants.gate_width("shared", q, dk))), q, dk,
+                                "shared").shape == (1, 1, 1, dk)
+    assert variants.gate_width("elementwise", q, dk) * dm == oracle.gate_param_count(dm, q, dk, "elementwise")
+    assert variants.gate_width("headwise", q, dk) * dm == oracle.gate_param_count(dm, q, dk, "headwise")
     for row in gold["rows"]:
         printed = row["params_M"]
         unit = 1.0 if float(printed).is_integer() else 0.1

@@ -272,7 +272,12 @@ VAR_SRC = os.path.join(os.path.dirname(SRC), "variants.py")
 VAR_MUTANTS = {
     "ns_sigmoid_half_only": ("return 0.5 + 0.5 * sigmoid(Z)", "return 0.5 * sigmoid(Z)"),
     "silu_without_input": ("return Z * sigmoid(Z)", "return sigmoid(Z)"),
-    "shared_over_dims_not_heads": ("return a.reshape(B, S, 1, D)", "return a.reshape(B, S, D, 1)"),
+    "shared_over_dims_not_heads": ("return a.reshape(B, S, Hq, D).sum(axis=2, keepdims=True) / Hq",
+                                   "return a.reshape(B, S, Hq, D).sum(axis=3, keepdims=True) / D"),
+    "shared_first_head_only": ("return a.reshape(B, S, Hq, D).sum(axis=2, keepdims=True) / Hq",
+                               "return a.reshape(B, S, Hq, D)[:, :, :1]"),
+    "shared_averages_logits": ("    g = gate_layout(activation(gate_scores(X, W), act), Hq, D, mode)\n",
+                               "    g = activation(gate_layout(gate_scores(X, W), Hq, D, mode), act)\n"),
     "rms_over_heads": ("np.mean(Y * Y, axis=-1, keepdims=True)", "np.mean(Y * Y, axis=-2, keepdims=True)"),
     "additive_as_multiplicative": ("        return Y + g\n", "        return Y * g\n"),
     "norm_after_gate": ("    if norm == \"rms\":\n        Y = rms_norm_heads(Y)\n", "    if norm == \"rms\":\n        Y = Y\n"),
@@ -298,7 +303,7 @@ def var_pins_pass(orc):
     try:
         for mode, act, combine, norm in CASES:
             B, S, Hq, Hkv, D, dm = 2, 4, 4, 2, 3, 4
-            N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+            N = {"elementwise": Hq * D, "headwise": Hq, "shared": Hq * D, "none": 1}[mode]
             t = draw(np.random.default_rng(11), B, S, Hq, Hkv, D, dm, N)
             got = orc.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
             if not np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12:

@@ -48,8 +48,13 @@ def brute_variant(t, mode, act, combine, norm):
                     if mode == "none":
                         out[b, i, h, d] = y[d]
                         continue
-                    col = {"elementwise": h * D + d, "headwise": h, "shared": d}[mode]
-                    g = f(math.fsum(X[b, i, k] * W[k, col] for k in range(dm)))
+                    if mode == "shared":
+                        # every head's activated score for dim d, averaged over the heads
+                        g = math.fsum(f(math.fsum(X[b, i, k] * W[k, hh * D + d] for k in range(dm)))
+                                      for hh in range(Hq)) / Hq
+                    else:
+                        col = {"elementwise": h * D + d, "headwise": h}[mode]
+                        g = f(math.fsum(X[b, i, k] * W[k, col] for k in range(dm)))
                     out[b, i, h, d] = y[d] * g if combine == "mul" else y[d] + g
     return out
 
@@ -63,7 +68,7 @@ CASES = [("elementwise", "ns_sigmoid", "mul", None), ("headwise", "sigmoid", "ad
 @pytest.mark.parametrize("mode,act,combine,norm", CASES)
 def test_matches_brute_force(mode, act, combine, norm):
     B, S, Hq, Hkv, D, dm = 2, 5, 4, 2, 3, 4
-    N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+    N = {"elementwise": Hq * D, "headwise": Hq, "shared": Hq * D, "none": 1}[mode]
     t = draw(np.random.default_rng(len(mode) + len(act)), B, S, Hq, Hkv, D, dm, N)
     got = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], mode, act, combine, norm)
     assert np.max(np.abs(got - brute_variant(t, mode, act, combine, norm))) <= 1e-12
@@ -74,7 +79,7 @@ def test_decode_shape_matches_brute_force(mode, act, combine, norm):
     """The same variants for one decode step: a single query per batch against a
     cache of L keys that holds it (the gate at the decode merge)."""
     B, L, Hq, Hkv, D, dm = 3, 7, 4, 2, 3, 4
-    N = {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 1}[mode]
+    N = {"elementwise": Hq * D, "headwise": Hq, "shared": Hq * D, "none": 1}[mode]
     rng = np.random.default_rng(7 + len(mode) + len(act))
     t = draw(rng, B, L, Hq, Hkv, D, dm, N)
     t["X"], t["Q"] = t["X"][:, -1:], t["Q"][:, -1:]          # the newest token queries the cache
@@ -110,13 +115,33 @@ def test_default_variant_is_the_g1_oracle_bitwise():
     assert np.array_equal(a, b)
 
 
-def test_shared_equals_elementwise_with_tiled_weight():
+def test_shared_equals_elementwise_when_heads_share_weights():
+    """With the same weight block for every head, all heads' scores are equal, so
+    their mean is that score: head-shared == elementwise."""
     rng = np.random.default_rng(2)
-    t = draw(rng, 1, 11, 4, 2, 4, 6, 4)
-    a = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "ns_sigmoid", "add")
-    Wt = np.tile(t["W"], (1, 4))                         # column h*D + d = column d, every head
+    Hq, D = 4, 4
+    t = draw(rng, 1, 11, Hq, 2, D, 6, D)
+    Wt = np.tile(t["W"], (1, Hq))                        # column h*D + d = column d, every head
+    a = ov.gated_sdpa_variant(t["X"], Wt, t["Q"], t["K"], t["V"], "shared", "ns_sigmoid", "add")
     b = ov.gated_sdpa_variant(t["X"], Wt, t["Q"], t["K"], t["V"], "elementwise", "ns_sigmoid", "add")
     assert np.max(np.abs(a - b)) <= 1e-15
+
+
+def test_shared_averages_activated_scores_not_logits():
+    """Two heads whose logits for a dimension are 4 and 0: the shared gate is
+    (σ(4) + σ(0)) / 2 = 0.7410..., not σ((4 + 0) / 2) = σ(2) = 0.8807...
+    (the mean of the activated scores, "GatedAttention [2025]" §1.3.2 (ii))."""
+    B, S, Hq, Hkv, D, dm = 1, 1, 2, 1, 1, 1
+    X = np.ones((B, S, dm))
+    W = np.array([[4.0, 0.0]])                            # head 0 logit 4, head 1 logit 0
+    Q = np.zeros((B, S, Hq, D)); K = np.zeros((B, S, Hkv, D)); V = np.ones((B, S, Hkv, D))
+    got = ov.gated_sdpa_variant(X, W, Q, K, V, "shared")  # Y = V = 1, so Y' is the gate
+    want = (1 / (1 + math.exp(-4.0)) + 0.5) / 2
+    assert abs(got[0, 0, 0, 0] - want) <= 1e-16 and abs(got[0, 0, 1, 0] - want) <= 1e-16
+    assert abs(want - 1 / (1 + math.exp(-2.0))) > 0.1
+    # with the identity activation the two readings coincide: the gate is the mean logit
+    got_id = ov.gated_sdpa_variant(X, W, Q, K, V, "shared", "identity")
+    assert got_id[0, 0, 0, 0] == 2.0
 
 
 def test_additive_with_zero_weight():
@@ -167,7 +192,7 @@ def test_value_gate_g2():
 
 
 def test_rows_subset_equals_full():
-    t = draw(np.random.default_rng(9), 2, 30, 4, 2, 4, 6, 4)
+    t = draw(np.random.default_rng(9), 2, 30, 4, 2, 4, 6, 16)
     full = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "silu", "add", "rms")
     rows = [0, 7, 29]
     part = ov.gated_sdpa_variant(t["X"], t["W"], t["Q"], t["K"], t["V"], "shared", "silu", "add", "rms", rows=rows)
