@@ -265,12 +265,17 @@ def variants_bench(args, torch, gsa, cfg):
     cases = [("elementwise", "sigmoid", "mul", None), ("elementwise", "ns_sigmoid", "mul", "rms"),
              ("elementwise", "silu", "add", None), ("shared", "sigmoid", "mul", None)]
     for layout, act, combine, norm in cases:
-        Wl = W if layout == "elementwise" else W[:, :cfg.D].contiguous()
+        # head-shared uses the elementwise-width W_θ and averages the activated
+        # scores over the heads (gsa_gate_head_mean) before the forward
+        Wl = W
         G = torch.empty((cfg.B * cfg.S, Wl.shape[1]), dtype=torch.float32, device="cuda:0")
+        Gs = torch.empty((cfg.B * cfg.S, cfg.D), dtype=torch.float32, device="cuda:0") if layout == "shared" else G
 
         def step():
             gsa.gate_logits(X, Wl, G=G, activation=act)
-            gsa.forward_variant(Q, K, V, G, layout, combine, norm, Y=Y)
+            if layout == "shared":
+                gsa.gate_head_mean(G, cfg.Hq, cfg.D, Gs=Gs)
+            gsa.forward_variant(Q, K, V, Gs, layout, combine, norm, Y=Y)
 
         ms, _, _ = time_steps(step, lambda: None, args.steps, args.warmup, torch)
         flops = cfg.attention_flops() + 2 * cfg.B * cfg.S * cfg.d_model * Wl.shape[1]

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libgsa.so")
-SOURCES = ["api.hip", "gate_gemm.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "gemm_bwd.hip", "attn_diag.hip", "value_gate.hip"]
+SOURCES = ["api.hip", "gate_gemm.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "gemm_bwd.hip", "attn_diag.hip", "value_gate.hip", "gate_shared.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -43,6 +43,7 @@ hipError_t launch_value_gate(const void* V, const float* G, void* Vout, int64_t 
                              bool headwise, bool bf16_inputs, hipStream_t st);
 hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
+hipError_t launch_gate_head_mean(const float* G, float* Gs, int64_t M, int Hq, int D, hipStream_t st);
 int bwd_stat_rows(int S);
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
                               int64_t N, hipStream_t st);
@@ -550,6 +551,23 @@ gsa_status gsa_value_gate(const void* V, const float* G, void* Vout, int64_t B, 
   return hip_result(gsa::launch_value_gate(V, G, Vout, B * S, (int)Hkv, (int)D, layout == GSA_GATE_HEADWISE,
                                            dtype == GSA_BF16, (hipStream_t)stream),
                     fn);
+}
+
+gsa_status gsa_gate_head_mean(const float* G, float* Gs, int64_t M, int64_t Hq, int64_t D, void* stream) {
+  const char* fn = "gsa_gate_head_mean";
+  if (!G || !Gs) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (M <= 0 || Hq <= 0 || D <= 0)
+    return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive (M=%lld Hq=%lld D=%lld)", fn, (long long)M,
+                (long long)Hq, (long long)D);
+  if (D % 4 != 0) return fail(GSA_ERR_UNSUPPORTED, "%s: D=%lld is not a multiple of 4", fn, (long long)D);
+  if (Hq > 4096 || D > 4096 || M > kIntMax || M * Hq * D > ((int64_t)1 << 40))
+    return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  if (!aligned16(G) || !aligned16(Gs)) return fail(GSA_ERR_MISALIGNED, "%s: G and Gs must be 16-byte aligned", fn);
+  const uintptr_t g0 = (uintptr_t)G, g1 = g0 + (uintptr_t)(M * Hq * D) * 4;
+  const uintptr_t s0 = (uintptr_t)Gs, s1 = s0 + (uintptr_t)(M * D) * 4;
+  if (s0 < g1 && g0 < s1) return fail(GSA_ERR_INVALID_ARG, "%s: G and Gs may not overlap", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_gate_head_mean(G, Gs, M, (int)Hq, (int)D, (hipStream_t)stream), fn);
 }
 
 gsa_status gsa_first_token_attention(const void* Q, const void* K, const float* LSE, float* F,

@@ -34,6 +34,59 @@ def _dtype(*ts):
     return _DTYPES[dt]
 
 
+def gate_width(layout, heads, D):
+    """Gate columns per token row for a layout: heads·D (elementwise), heads
+    (headwise) or D (shared: the head-mean of an elementwise gate)."""
+    return {"elementwise": heads * D, "headwise": heads, "shared": D}[layout]
+
+
+def _check_gate(G, layout, rows, heads, D, ref, name="G"):
+    """The gate tensor the kernels will read: None exactly when layout is
+    "none", else a contiguous float32 tensor on ref's device holding
+    rows × gate_width(layout, heads, D) values.  Returns G (the caller takes its
+    device pointer after every other check).
+    The C ABI cannot see sizes, so this is where a gate of the wrong width or
+    dtype is refused before any launch."""
+    if layout == "none":
+        if G is not None:
+            raise ValueError(f"{name} must be None when there is no gate")
+        return None
+    if G is None:
+        raise ValueError(f"{name} is required for the {layout!r} gate")
+    if not isinstance(G, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if G.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {G.dtype})")
+    if G.device != ref.device:
+        raise ValueError(f"{name} is on {G.device}, the other tensors on {ref.device}")
+    width = gate_width(layout, heads, D)
+    if G.numel() != rows * width:
+        raise ValueError(f"{name} has {G.numel()} values; the {layout!r} gate needs {rows} rows x {width}")
+    return G
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _out(Y, like, name="Y"):
+    """A caller-supplied output must match `like` (shape, dtype, device); None allocates one."""
+    if Y is None:
+        return torch.empty_like(like)
+    if not isinstance(Y, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(Y.shape) != tuple(like.shape) or Y.dtype != like.dtype or Y.device != like.device:
+        raise ValueError(f"{name} must be {tuple(like.shape)} {like.dtype} on {like.device} "
+                         f"(got {tuple(Y.shape)} {Y.dtype} on {Y.device})")
+    return Y
+
+
+def _same_device(ref, **ts):
+    for n, t in ts.items():
+        if isinstance(t, torch.Tensor) and t.device != ref.device:
+            raise ValueError(f"{n} is on {t.device}, the other tensors on {ref.device}")
+
+
 ACTIVATIONS = {"identity": _lib.GSA_ACT_IDENTITY, "sigmoid": _lib.GSA_ACT_SIGMOID,
                "ns_sigmoid": _lib.GSA_ACT_NS_SIGMOID, "silu": _lib.GSA_ACT_SILU}
 
@@ -50,10 +103,12 @@ def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, stream=None):
     N = W.shape[1]
     if W.shape[0] != dm:
         raise ValueError(f"W has {W.shape[0]} rows, X has d_model={dm}")
+    _same_device(X, W=W)
     if G is None:
         G = torch.empty((M, N), dtype=torch.float32, device=X.device)
-    elif G.dtype != torch.float32 or G.numel() != M * N:
-        raise ValueError("G must be float32 with M*N elements")
+    elif not isinstance(G, torch.Tensor) or G.dtype != torch.float32 or G.numel() != M * N \
+            or G.device != X.device:
+        raise ValueError(f"G must be float32 with M*N = {M * N} elements on {X.device}")
     lib = _lib.load()
     if activation is None:
         act = _lib.GSA_ACT_SIGMOID if apply_sigmoid else _lib.GSA_ACT_IDENTITY
@@ -64,6 +119,11 @@ def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, stream=None):
     _lib.check(lib.gsa_gate_logits(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N,
                                    _dtype(X, W), act, _stream(stream)))
     return G
+
+
+def _layout_of_mode(mode):
+    _mode(mode)
+    return mode
 
 
 def _mode(mode):
@@ -78,11 +138,11 @@ def forward(Q, K, V, G, mode, Y=None, stream=None):
     Hkv = K.shape[2]
     if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
         raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
-    if Y is None:
-        Y = torch.empty_like(Q)
-    gp = None if G is None else _dev(G, "G")
+    _same_device(Q, K=K, V=V)
+    G = _check_gate(G, _layout_of_mode(mode), B * S, Hq, D, Q)
+    Y = _out(Y, Q)
     lib = _lib.load()
-    _lib.check(lib.gsa_forward(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), gp, _dev(Y, "Y"),
+    _lib.check(lib.gsa_forward(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _opt(G, "G"), _dev(Y, "Y"),
                                B, S, Hq, Hkv, D, _mode(mode), _dtype(Q, K, V, Y), _stream(stream)))
     return Y
 
@@ -93,15 +153,15 @@ def forward_lse(Q, K, V, G, mode, Y=None, LSE=None, stream=None):
     Hkv = K.shape[2]
     if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
         raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
-    if Y is None:
-        Y = torch.empty_like(Q)
+    _same_device(Q, K=K, V=V, LSE=LSE)
+    G = _check_gate(G, _layout_of_mode(mode), B * S, Hq, D, Q)
+    Y = _out(Y, Q)
     if LSE is None:
         LSE = torch.empty((B, Hq, S), dtype=torch.float32, device=Q.device)
     elif LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S:
         raise ValueError("LSE must be float32 with B*Hq*S elements")
-    gp = None if G is None else _dev(G, "G")
     lib = _lib.load()
-    _lib.check(lib.gsa_forward_lse(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), gp, _dev(Y, "Y"),
+    _lib.check(lib.gsa_forward_lse(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _opt(G, "G"), _dev(Y, "Y"),
                                    _dev(LSE, "LSE"), B, S, Hq, Hkv, D, _mode(mode),
                                    _dtype(Q, K, V, Y), _stream(stream)))
     return Y, LSE
@@ -123,16 +183,16 @@ def decode(Q, Kc, Vc, G, mode, num_splits=0, Y=None, workspace=None, stream=None
     L, Hkv = Kc.shape[1], Kc.shape[2]
     if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
         raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
-    if Y is None:
-        Y = torch.empty_like(Q)
+    _same_device(Q, Kc=Kc, Vc=Vc, workspace=workspace)
+    G = _check_gate(G, _layout_of_mode(mode), B, Hq, D, Q)
+    Y = _out(Y, Q)
     need = decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     wp = None if workspace is None else _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    gp = None if G is None else _dev(G, "G")
     lib = _lib.load()
-    _lib.check(lib.gsa_decode(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), gp, _dev(Y, "Y"),
+    _lib.check(lib.gsa_decode(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), _opt(G, "G"), _dev(Y, "Y"),
                               B, L, Hq, Hkv, D, _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits,
                               wp, wbytes, _stream(stream)))
     return Y
@@ -153,11 +213,13 @@ def decode_noalloc(Q, Kc, Vc, G, mode, Y, num_splits=0, stream=None):
     L, Hkv = Kc.shape[1], Kc.shape[2]
     if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
         raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
-    if Y is None or Y.shape != Q.shape:
-        raise ValueError("Y must be given, with Q's shape")
-    gp = None if G is None else _dev(G, "G")
+    if Y is None:
+        raise ValueError("decode_noalloc allocates nothing: pass the output Y")
+    _same_device(Q, Kc=Kc, Vc=Vc)
+    G = _check_gate(G, _layout_of_mode(mode), B, Hq, D, Q)
+    Y = _out(Y, Q)
     lib = _lib.load()
-    _lib.check(lib.gsa_decode_noalloc(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), gp, _dev(Y, "Y"),
+    _lib.check(lib.gsa_decode_noalloc(_dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), _opt(G, "G"), _dev(Y, "Y"),
                                       B, L, Hq, Hkv, D, _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits,
                                       _stream(stream)))
     return Y
@@ -184,10 +246,16 @@ def backward(X, W, G, Q, K, V, Y, LSE, dY, mode, workspace=None, stream=None):
         raise ValueError("Y and dY must have Q's shape")
     if LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S:
         raise ValueError("LSE must be float32 with B*Hq*S elements")
-    gated = mode != "none"
+    gated = _mode(mode) != _lib.GSA_GATE_NONE
+    _same_device(Q, K=K, V=V, Y=Y, LSE=LSE, dY=dY, X=X, W=W, workspace=workspace)
+    _check_gate(G, mode, B * S, Hq, D, Q)
+    if not gated and (X is not None or W is not None):
+        raise ValueError("X and W must be None without a gate")
     d_model = X.shape[-1] if gated else 0
-    if gated and (W.shape[0] != d_model or X.numel() != B * S * d_model):
-        raise ValueError("X must hold B*S rows of d_model and W must be [d_model, N]")
+    if gated and (W.dim() != 2 or W.shape[0] != d_model or X.numel() != B * S * d_model
+                  or W.shape[1] != gate_width(mode, Hq, D)):
+        raise ValueError(f"X must hold B*S = {B * S} rows of d_model and W must be [d_model, "
+                         f"{gate_width(mode, Hq, D)}] for the {mode!r} gate")
     need = backward_workspace_bytes(B, S, Hq, Hkv, D, d_model, mode)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
@@ -218,11 +286,14 @@ def forward_variant(Q, K, V, G, layout, combine="mul", norm=None, Y=None, LSE=No
         raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
     if layout not in LAYOUTS or combine not in ("mul", "add") or norm not in (None, "rms"):
         raise ValueError("layout, combine or norm not recognised")
-    if Y is None:
-        Y = torch.empty_like(Q)
+    _same_device(Q, K=K, V=V, LSE=LSE)
+    G = _check_gate(G, layout, B * S, Hq, D, Q)
+    Y = _out(Y, Q)
+    if LSE is not None and (LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S):
+        raise ValueError("LSE must be float32 with B*Hq*S elements")
     lib = _lib.load()
     _lib.check(lib.gsa_forward_variant(
-        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), None if G is None else _dev(G, "G"), _dev(Y, "Y"),
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _opt(G, "G"), _dev(Y, "Y"),
         None if LSE is None else _dev(LSE, "LSE"), B, S, Hq, Hkv, D, LAYOUTS[layout],
         _lib.GSA_COMBINE_ADD if combine == "add" else _lib.GSA_COMBINE_MUL,
         _lib.GSA_NORM_RMS if norm == "rms" else _lib.GSA_NORM_NONE, _dtype(Q, K, V, Y), _stream(stream)))
@@ -242,8 +313,9 @@ def decode_variant(Q, Kc, Vc, G, layout, combine="mul", norm=None, num_splits=0,
         raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
     if layout not in LAYOUTS or combine not in ("mul", "add") or norm not in (None, "rms"):
         raise ValueError("layout, combine or norm not recognised")
-    if Y is None:
-        Y = torch.empty_like(Q)
+    _same_device(Q, Kc=Kc, Vc=Vc, workspace=workspace)
+    G = _check_gate(G, layout, B, Hq, D, Q)
+    Y = _out(Y, Q)
     need = decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits) if Q.dtype == torch.bfloat16 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
@@ -251,7 +323,7 @@ def decode_variant(Q, Kc, Vc, G, layout, combine="mul", norm=None, num_splits=0,
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = _lib.load()
     _lib.check(lib.gsa_decode_variant(
-        _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), None if G is None else _dev(G, "G"), _dev(Y, "Y"),
+        _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), _opt(G, "G"), _dev(Y, "Y"),
         B, L, Hq, Hkv, D, LAYOUTS[layout], _lib.GSA_COMBINE_ADD if combine == "add" else _lib.GSA_COMBINE_MUL,
         _lib.GSA_NORM_RMS if norm == "rms" else _lib.GSA_NORM_NONE, _dtype(Q, Kc, Vc, Y), num_splits, wp, wbytes,
         _stream(stream)))
@@ -262,10 +334,12 @@ def value_gate(V, G, layout, Vout=None, stream=None):
     """G2: V ⊙ G per key/value head (elementwise G [B*S, Hkv*D]) or per head
     (headwise G [B*S, Hkv]); returns the gated values, V's shape and dtype."""
     B, S, Hkv, D = V.shape
-    if Vout is None:
-        Vout = torch.empty_like(V)
+    if layout not in ("elementwise", "headwise"):
+        raise ValueError("the value gate's layout is 'elementwise' or 'headwise'")
+    G = _check_gate(G, layout, B * S, Hkv, D, V)
+    Vout = _out(Vout, V, "Vout")
     lib = _lib.load()
-    _lib.check(lib.gsa_value_gate(_dev(V, "V"), _dev(G, "G"), _dev(Vout, "Vout"), B, S, Hkv, D,
+    _lib.check(lib.gsa_value_gate(_dev(V, "V"), _opt(G, "G"), _dev(Vout, "Vout"), B, S, Hkv, D,
                                   LAYOUTS[layout], _dtype(V, Vout), _stream(stream)))
     return Vout
 
@@ -308,13 +382,62 @@ def first_token_attention(Q, K, LSE, with_means=True, stream=None):
     return (F, means) if with_means else F
 
 
+def _check_gate_inputs(X, W, rows, Hq, D, mode):
+    """X must hold `rows` token rows and W_θ must have the gate width of `mode`."""
+    if _mode(mode) == _lib.GSA_GATE_NONE:
+        return
+    if X is None or W is None:
+        raise ValueError(f"X and W are required for the {mode!r} gate")
+    dm = X.shape[-1]
+    if X.numel() != rows * dm:
+        raise ValueError(f"X must hold {rows} token rows of d_model (got shape {tuple(X.shape)})")
+    if W.dim() != 2 or W.shape[0] != dm or W.shape[1] != gate_width(mode, Hq, D):
+        raise ValueError(f"W must be [d_model={dm}, {gate_width(mode, Hq, D)}] for the {mode!r} gate "
+                         f"(got {tuple(W.shape)})")
+
+
+def gate_head_mean(G, Hq, D, Gs=None, stream=None):
+    """Head-shared gate scores Gs [M, D] = the mean over the Hq heads of the
+    activated elementwise scores G [M, Hq·D] (float32)."""
+    if not isinstance(G, torch.Tensor) or G.dtype != torch.float32:
+        raise TypeError("G must be a float32 torch.Tensor")
+    if G.numel() % (Hq * D) != 0:
+        raise ValueError(f"G must hold rows of Hq*D = {Hq * D} values")
+    M = G.numel() // (Hq * D)
+    if Gs is None:
+        Gs = torch.empty((M, D), dtype=torch.float32, device=G.device)
+    elif Gs.dtype != torch.float32 or Gs.numel() != M * D or Gs.device != G.device:
+        raise ValueError(f"Gs must be float32 with M*D = {M * D} values on {G.device}")
+    lib = _lib.load()
+    _lib.check(lib.gsa_gate_head_mean(_dev(G, "G"), _dev(Gs, "Gs"), M, Hq, D, _stream(stream)))
+    return Gs
+
+
 def gated_attention(X, W, Q, K, V, mode, stream=None):
     """The whole prefill path: gate projection + sigmoid, then causal gated SDPA."""
+    B, S, Hq, D = Q.shape
+    _check_gate_inputs(X, W, B * S, Hq, D, mode)
     G = None if mode == "none" else gate_logits(X, W, stream=stream)
     return forward(Q, K, V, G, mode, stream=stream)
 
 
 def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, stream=None):
     """The whole decode path: gate projection + sigmoid for the new token, then decode."""
+    B, _, Hq, D = Q.shape
+    _check_gate_inputs(X, W, B, Hq, D, mode)
     G = None if mode == "none" else gate_logits(X, W, stream=stream)
     return decode(Q, Kc, Vc, G, mode, num_splits=num_splits, stream=stream)
+
+
+def gated_attention_variant(X, W, Q, K, V, layout, activation="sigmoid", combine="mul", norm=None, stream=None):
+    """A design-space point of the whole prefill path: G = act(X·W_θ), then for
+    the head-shared layout the mean over the heads (W_θ is Hq·D wide, as for
+    elementwise), then the variant forward combine(norm(Y), G)."""
+    B, S, Hq, D = Q.shape
+    if layout == "none":
+        return forward_variant(Q, K, V, None, "none", combine, norm, stream=stream)
+    _check_gate_inputs(X, W, B * S, Hq, D, "elementwise" if layout == "shared" else layout)
+    G = gate_logits(X, W, activation=activation, stream=stream)
+    if layout == "shared":
+        G = gate_head_mean(G, Hq, D, stream=stream)
+    return forward_variant(Q, K, V, G, layout, combine, norm, stream=stream)

@@ -58,7 +58,8 @@ typedef enum gsa_gate_mode {
   GSA_GATE_ELEMENTWISE = 1,  /* G is [rows, Hq*D]; column h*D + d gates head h, dim d */
   GSA_GATE_HEADWISE = 2,     /* G is [rows, Hq];   column h gates all of head h       */
   GSA_GATE_SHARED = 3        /* G is [rows, D];    column d gates dim d of every head
-                                (gsa_forward_variant and gsa_decode_variant only) */
+                                (gsa_forward_variant and gsa_decode_variant only; the
+                                head-shared score is gsa_gate_head_mean's output) */
 } gsa_gate_mode;
 
 /* Gate activation applied by gsa_gate_logits ("GatedAttention [2025]" §1.2.2
@@ -261,6 +262,19 @@ gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, cons
 gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,
                               int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int layout, int combine, int norm,
                               int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Head-shared gate scores ("GatedAttention [2025]" §1.2.2 item (3)b; the §1.3.2
+ * Table 1 discussion, observation (ii), averages the n×q×d_k gating scores
+ * over the q query heads into one n×d_k score; "10 · 门控" §3.2 Table 1 row 12):
+ *   Gs[m, d] = (1/Hq) · Σ_{h<Hq} G[m, h·D + d]     (heads summed in order, float32)
+ *   G  : [M, Hq·D] float32, the activated scores gsa_gate_logits wrote for a
+ *        q·d_k-wide W_θ (the mean is taken after the activation)
+ *   Gs : [M, D] float32 output, the gate of layout GSA_GATE_SHARED for
+ *        gsa_forward_variant and gsa_decode_variant.  G and Gs may not overlap.
+ * Requires D % 4 == 0, Hq and D at most 4096; both pointers 16-byte aligned.
+ */
+gsa_status gsa_gate_head_mean(const float* G, float* Gs, int64_t M, int64_t Hq, int64_t D, void* stream);
 
 /*
  * G2 value gating ("GatedAttention [2025]" §1.2.2, position G2): the gate

@@ -287,6 +287,22 @@ def test_project_qkvg_argument_checks(lib):
     assert lib.gsa_last_error_message().decode().startswith("gsa_project_qkvg")
 
 
+def test_gate_head_mean_argument_checks(lib):
+    def hm(G=FAKE, Gs=FAKE + (1 << 24), M=8, Hq=4, D=64):
+        return lib.gsa_gate_head_mean(G, Gs, M, Hq, D, None)
+    assert hm(G=None) == _lib.GSA_ERR_INVALID_ARG
+    assert hm(M=0) == _lib.GSA_ERR_INVALID_ARG
+    assert hm(Hq=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert hm(D=6) == _lib.GSA_ERR_UNSUPPORTED
+    assert hm(Hq=5000) == _lib.GSA_ERR_UNSUPPORTED
+    assert hm(Gs=FAKE + (1 << 24) + 4) == _lib.GSA_ERR_MISALIGNED
+    assert hm(Gs=FAKE + 16) == _lib.GSA_ERR_INVALID_ARG          # overlaps G
+    assert hm(Gs=FAKE) == _lib.GSA_ERR_INVALID_ARG
+    if not have_gpu():
+        assert hm() == _lib.GSA_ERR_NO_DEVICE
+        assert hm(Gs=FAKE + 8 * 4 * 64 * 4) == _lib.GSA_ERR_NO_DEVICE   # right after G
+
+
 def test_first_token_attention_argument_checks(lib):
     def fa(Q=FAKE, K=FAKE, LSE=FAKE, F=FAKE, hm=None, B=1, S=8, Hq=4, Hkv=2, D=128, dtype=1):
         return lib.gsa_first_token_attention(Q, K, LSE, F, hm, B, S, Hq, Hkv, D, dtype, None)

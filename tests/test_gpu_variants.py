@@ -1,6 +1,7 @@
 """The gate design-space variants on the GPU against the fp64 oracle: gate
-activations (gsa_gate_logits), layouts / combine / norm (gsa_forward_variant)
-and G2 value gating (gsa_value_gate + gsa_forward)."""
+activations (gsa_gate_logits), the head-shared gate (gsa_gate_head_mean: the
+mean over the heads of the activated elementwise scores), layouts / combine /
+norm (gsa_forward_variant) and G2 value gating (gsa_value_gate + gsa_forward)."""
 import math
 
 import numpy as np
@@ -38,6 +39,45 @@ def test_gate_activations(M, dm, N, dtype, act):
     report(G.cpu().numpy(), want, tol, f"{act} {M}x{dm}x{N}")
 
 
+@pytest.mark.parametrize("act", ["sigmoid", "identity", "silu"])
+@pytest.mark.parametrize("M,Hq,D", [(1, 1, 4), (37, 4, 64), (8192, 16, 128), (64, 32, 128), (5, 3, 12)])
+def test_gate_head_mean(M, Hq, D, act):
+    """Gs = mean over the Hq heads of the activated scores, against the oracle's
+    head-shared layout (float32 sums of Hq values: relative error ≤ Hq·2^-24)."""
+    dm = 64
+    X, W = draw_xw(M, dm, Hq * D, torch.bfloat16, seed=M + Hq)
+    G = gsa.gate_logits(X, W, activation=act)
+    Gs, guard = guarded_empty((M, D), torch.float32, DEV)
+    gsa.gate_head_mean(G, Hq, D, Gs=Gs)
+    torch.cuda.synchronize()
+    assert guard_ok(guard), "write past the end of Gs"
+    a = ov.activation(oracle.gate_scores(f64(X), f64(W)), act)[None]          # [1, M, Hq*D]
+    want = ov.gate_layout(a, Hq, D, "shared").reshape(M, D)
+    tol = 1e-4 * max(1.0, float(np.abs(a).max()))
+    report(Gs.cpu().numpy(), want, tol, f"head mean {act} M{M} Hq{Hq} D{D}")
+
+
+@pytest.mark.parametrize("Hq", [2, 8])
+def test_head_mean_of_identical_heads(Hq):
+    """With the same weight block for every head, every head's score is the same
+    float32 value x, and the gate is the mean of Hq copies of x.  For two heads
+    x + x = 2x and 2x / 2 = x exactly, so head-shared equals the head bitwise;
+    summing more copies in order rounds (3x needs one more bit), so for eight
+    the mean is within 8·2^-24 of x relatively."""
+    D, M, dm = 64, 300, 128
+    X, W = draw_xw(M, dm, D, torch.bfloat16, seed=4)
+    G = gsa.gate_logits(X, W.repeat(1, Hq))
+    Gs = gsa.gate_head_mean(G, Hq, D)
+    torch.cuda.synchronize()
+    x = G[:, :D]
+    for h in range(1, Hq):
+        assert torch.equal(G[:, h * D:(h + 1) * D], x)       # the GEMM gives every head block the same values
+    if Hq == 2:
+        assert torch.equal(Gs, x)
+    else:
+        assert float(((Gs - x).abs() / x.abs()).max()) <= Hq * 2.0 ** -24
+
+
 ACT_FOR = {("mul", "elementwise"): "sigmoid", ("mul", "headwise"): "ns_sigmoid", ("mul", "shared"): "sigmoid",
            ("add", "elementwise"): "silu", ("add", "headwise"): "sigmoid", ("add", "shared"): "identity"}
 CASES = [(layout, combine, norm) for layout in ("elementwise", "headwise", "shared")
@@ -45,7 +85,14 @@ CASES = [(layout, combine, norm) for layout in ("elementwise", "headwise", "shar
 
 
 def gate_width(layout, Hq, D):
-    return {"elementwise": Hq * D, "headwise": Hq, "shared": D, "none": 0}[layout]
+    """Columns of W_θ: head-shared uses the elementwise width and averages the
+    activated scores over the heads (gsa_gate_head_mean)."""
+    return {"elementwise": Hq * D, "headwise": Hq, "shared": Hq * D, "none": 0}[layout]
+
+
+def gate_for(X, W, layout, act, Hq, D):
+    G = gsa.gate_logits(X, W, activation=act)
+    return gsa.gate_head_mean(G, Hq, D) if layout == "shared" else G
 
 
 def run_variant(cfg, layout, combine, norm, seed, rows=None):
@@ -56,7 +103,7 @@ def run_variant(cfg, layout, combine, norm, seed, rows=None):
     if N:
         gx = torch.Generator(device=DEV).manual_seed(seed + 5)
         W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
-        G = gsa.gate_logits(inp["X"], W, activation=act)
+        G = gate_for(inp["X"], W, layout, act, cfg.Hq, cfg.D)
     Y = gsa.forward_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm)
     torch.cuda.synchronize()
     want = ov.gated_sdpa_variant(f64(inp["X"]), None if W is None else f64(W), f64(inp["Q"]), f64(inp["K"]),
@@ -131,7 +178,7 @@ def run_decode_variant(B, L, Hq, Hkv, D, dtype, layout, combine, norm, seed, num
     if N:
         gx = torch.Generator(device=DEV).manual_seed(seed + 5)
         W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
-        G = gsa.gate_logits(inp["X"].reshape(B, cfg.d_model), W, activation=act)
+        G = gate_for(inp["X"].reshape(B, cfg.d_model), W, layout, act, Hq, D)
     Y, guard = guarded_empty(tuple(inp["Q"].shape), inp["Q"].dtype, DEV)
     gsa.decode_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm, num_splits=num_splits, Y=Y)
     torch.cuda.synchronize()
@@ -182,7 +229,7 @@ def test_decode_variant_full_size_sampled(layout, combine, norm):
     act = ACT_FOR[(combine, layout)]
     gx = torch.Generator(device=DEV).manual_seed(7)
     W = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
-    G = gsa.gate_logits(inp["X"].reshape(cfg.B, cfg.d_model), W, activation=act)
+    G = gate_for(inp["X"].reshape(cfg.B, cfg.d_model), W, layout, act, cfg.Hq, cfg.D)
     Y = gsa.decode_variant(inp["Q"], inp["K"], inp["V"], G, layout, combine, norm)
     torch.cuda.synchronize()
     assert not torch.isnan(Y.float()).any()
