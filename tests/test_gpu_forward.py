@@ -9,7 +9,7 @@ import torch
 import oracle
 import gated_softmax_attention_amd as gsa
 from synth import CONFIGS, make_inputs
-from helpers import TOL, f64, report, guarded_empty, guard_ok, oracle_rows, sample_rows
+from helpers import TOL, f64, report, guarded_empty, guard_ok, oracle_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -159,26 +159,30 @@ def test_headwise_equals_broadcast_elementwise():
     assert torch.equal(Yh.view(torch.int16), Ye.view(torch.int16))
 
 
-# --------------------------------------------------------------- full-size configs, sampled rows
-@pytest.mark.parametrize("name", ["dense_prefill", "gqa_prefill", "long_prefill"])
-def test_full_size_config_sampled_rows(name):
-    cfg = CONFIGS[name]
-    print(f"  {name}: generating inputs", flush=True)
-    inp = make_inputs(cfg, seed=0, device=DEV)
-    Y, G = run(inp, cfg.mode, guard=False)
-    rows = sample_rows(cfg.S)
-    idx = torch.tensor(rows, device=DEV)
-    want = oracle_rows(f64(inp["X"][:, idx]), f64(inp["W"]), f64(inp["Q"][:, idx]),
-                       f64(inp["K"]), f64(inp["V"]), cfg.mode, rows)
-    got = f64(Y[:, idx])
-    report(got, want, TOL[cfg.dtype], f"{name} rows {len(rows)}")
-    # row 0 of every (batch, head) at full size: exactly V[0] times the gate
+# --------------------------------------------------------------- full-size configs
+def check_row0(cfg, inp, Y, G):
+    """Row 0 of every (batch, head): a softmax over one key is 1, so the output is
+    exactly V[0] times the gate, rounded once (bitwise)."""
     grp = cfg.group
     v0 = inp["V"][:, 0].float().repeat_interleave(grp, dim=1)
     g0 = G.view(cfg.B, cfg.S, -1)[:, 0]
     g0 = g0.view(cfg.B, cfg.Hq, cfg.D) if cfg.mode == "elementwise" else g0.view(cfg.B, cfg.Hq, 1)
     assert torch.equal(Y[:, 0].view(torch.int16), (v0 * g0).to(torch.bfloat16).view(torch.int16))
-    assert not torch.isnan(Y.float()).any()
+
+
+@pytest.mark.parametrize("name", ["dense_prefill", "gqa_prefill", "long_prefill"])
+def test_full_size_config_every_element(name):
+    """The dense (B 2, S 4096, 16/16 heads, elementwise gate), GQA (B 1, S 8192,
+    32/4 heads, headwise gate) and 32k (B 1, S 32768, 16/2 heads, token-0 keys
+    ×8, elementwise gate) prefill workloads in the launch the bench times: every
+    output element against one oracle evaluation, max-abs ≤ 2e-2; row 0 bitwise."""
+    cfg = CONFIGS[name]
+    print(f"  {name}: generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=0, device=DEV)
+    Y, G = run(inp, cfg.mode)
+    check_row0(cfg, inp, Y, G)
+    print(f"  {name}: oracle over all {cfg.B * cfg.S} rows", flush=True)
+    report(f64(Y), full_oracle(inp, cfg.mode), TOL[cfg.dtype], f"{name} every element")
 
 
 # --------------------------------------------------------------- extremes
