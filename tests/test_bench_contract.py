@@ -23,7 +23,8 @@ def test_more_than_one_gpu_is_refused():
 def test_bench_json_line():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "2",
                         "--no-cpu-baseline", "--no-decode", "--no-backward", "--no-projection", "--no-variants",
-                        "--no-diagnostic", "--no-others"], capture_output=True, text=True, timeout=280, cwd=ROOT)
+                        "--no-diagnostic", "--no-others", "--settle", "0.05", "--blocks", "3"], capture_output=True, text=True,
+                       timeout=280, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1, r.stdout[-2000:]
@@ -39,3 +40,9 @@ def test_bench_json_line():
         assert k in rf, k
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    # achieved follows from the event-timed average launch duration of the forward
+    assert abs(rf["achieved"] - rf["algorithmic_flops_per_launch"] / (rf["avg_launch_ms"] * 1e-3) / 1e12) < 1e-6
+    t = d["timing"]
+    assert t["min_ms"] <= t["median_ms"] and t["clock_settle_s"] >= 0 and t["blocks"] >= 1
+    assert set(d["workloads"]) == {"dense_prefill"}
+    assert d["workloads"]["dense_prefill"]["value"] == d["value"]
