@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <initializer_list>
 #include <string>
 
 #include "gsa.h"
@@ -75,6 +76,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kIntMax = 0x7fffffff;
 
+// The product of non-negative sizes is at most lim, computed without
+// overflowing (a product that does not fit int64 is not at most lim).  Every
+// size check multiplies through this, so arbitrary int64 arguments cannot make
+// the checks themselves overflow.
+bool prod_le(std::initializer_list<int64_t> xs, int64_t lim) {
+  int64_t p = 1;
+  for (int64_t x : xs) {
+    if (x < 0 || __builtin_mul_overflow(p, x, &p)) return false;
+  }
+  return p <= lim;
+}
+constexpr int64_t kElemMax = (int64_t)1 << 40;   // no tensor of more elements fits a GPU
+
 // Per-device check that the device is a gfx950 part, done once per device.
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -136,11 +150,11 @@ gsa_status check_attn_shape(const char* fn, int64_t B, int64_t S, int64_t Hq, in
     return fail(GSA_ERR_INVALID_ARG, "%s: G must be NULL exactly when mode is GSA_GATE_NONE", fn);
   if (D != 64 && D != 128)
     return fail(GSA_ERR_UNSUPPORTED, "%s: head dim %lld is not supported (64 or 128)", fn, (long long)D);
-  if (B * S > kIntMax || Hq > 4096 || Hkv > 4096 || S > kIntMax)
+  if (!prod_le({B, S}, kIntMax) || Hq > 4096 || Hkv > 4096)
     return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
   // the kernels address one batch's Q / K / V rows with 32-bit byte offsets
   // (bounded here at the float32 size)
-  if (Sq * Hq * D * 4 > kIntMax || S * Hkv * D * 4 > kIntMax)
+  if (!prod_le({Sq, Hq, D, 4}, kIntMax) || !prod_le({S, Hkv, D, 4}, kIntMax))
     return fail(GSA_ERR_UNSUPPORTED, "%s: one batch of Q or K/V exceeds 2 GiB", fn);
   return GSA_OK;
 }
@@ -178,7 +192,8 @@ gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, in
   if (d_model % 8 != 0)
     return fail(GSA_ERR_UNSUPPORTED, "gsa_gate_logits: d_model=%lld is not a multiple of 8",
                 (long long)d_model);
-  if (M > kIntMax || d_model > kIntMax || N > kIntMax)
+  if (M > kIntMax || d_model > kIntMax || N > kIntMax || !prod_le({M, d_model}, kElemMax) ||
+      !prod_le({d_model, N}, kElemMax) || !prod_le({M, N}, kElemMax))
     return fail(GSA_ERR_UNSUPPORTED, "gsa_gate_logits: sizes exceed the supported range");
   if (!aligned16(X) || !aligned16(W) || !aligned16(G))
     return fail(GSA_ERR_MISALIGNED, "gsa_gate_logits: X, W and G must be 16-byte aligned");
@@ -221,6 +236,7 @@ gsa_status gsa_forward_lse(const void* Q, const void* K, const void* V, const fl
 
 int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int num_splits) {
   if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || num_splits < 0) return 0;
+  if (!prod_le({B, L}, kIntMax) || Hq > 4096 || D > 4096) return 0;   // gsa_decode's range
   int64_t ns = num_splits > 0 ? num_splits : gsa::decode_auto_splits(B, L, Hq, Hkv);
   if (ns > L) ns = L;
   // every split gets at least one key: the effective count after rounding the chunk
@@ -231,7 +247,7 @@ int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int
 size_t gsa_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
                                   int num_splits) {
   const int64_t ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
-  if (ns == 0) return 0;
+  if (ns == 0 || !prod_le({B, Hq, ns, D + 4, (int64_t)sizeof(float)}, kElemMax)) return 0;
   return (size_t)(B * Hq * ns * (D + 4)) * sizeof(float);
 }
 
@@ -242,7 +258,7 @@ gsa_status gsa_decode(const void* Q, const void* Kc, const void* Vc, const float
   if (gsa_status st = check_attn_shape("gsa_decode", B, L, Hq, Hkv, D, mode, G, 1)) return st;
   if (gsa_status st = check_dtype("gsa_decode", dtype)) return st;
   if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "gsa_decode: num_splits must be >= 0");
-  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "gsa_decode: B*L exceeds the supported range");
+  if (!prod_le({B, L}, kIntMax)) return fail(GSA_ERR_UNSUPPORTED, "gsa_decode: B*L exceeds the supported range");
   if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
     return fail(GSA_ERR_MISALIGNED, "gsa_decode: Q, Kc, Vc, G and Y must be 16-byte aligned");
   size_t need = 0;
@@ -312,7 +328,7 @@ gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, con
   if (gsa_status st = check_attn_shape(fn, B, L, Hq, Hkv, D, mode, G, 1)) return st;
   if (gsa_status st = check_dtype(fn, dtype)) return st;
   if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
-  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
+  if (!prod_le({B, L}, kIntMax)) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
   if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
     return fail(GSA_ERR_MISALIGNED, "%s: Q, Kc, Vc, G and Y must be 16-byte aligned", fn);
   int64_t ns = 0;
@@ -359,7 +375,7 @@ gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, con
     return st;
   if (gsa_status st = check_dtype(fn, dtype)) return st;
   if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
-  if (B * L > kIntMax) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
+  if (!prod_le({B, L}, kIntMax)) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
   if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (G && !aligned16(G)))
     return fail(GSA_ERR_MISALIGNED, "%s: Q, Kc, Vc, G and Y must be 16-byte aligned", fn);
   int64_t ns = 0;
@@ -428,7 +444,7 @@ size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hk
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
   if (mode != GSA_GATE_NONE && mode != GSA_GATE_ELEMENTWISE && mode != GSA_GATE_HEADWISE) return 0;
   if (mode != GSA_GATE_NONE && d_model <= 0) return 0;
-  if (B * S > kIntMax || Hq > 4096 || D > 128 || d_model > kIntMax) return 0;
+  if (!prod_le({B, S}, kIntMax) || Hq > 4096 || D > 128 || d_model > kIntMax) return 0;
   return bwd_layout(B, S, Hq, Hkv, D, d_model, mode).total;
 }
 
@@ -453,7 +469,7 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
     if (d_model % 8 != 0 || N % 8 != 0)
       return fail(GSA_ERR_UNSUPPORTED, "%s: d_model=%lld and the gate width %lld must be multiples of 8", fn,
                   (long long)d_model, (long long)N);
-    if (M * d_model * 2 > kU32Bytes || M * N * 2 > kU32Bytes || d_model * N * 4 > kU32Bytes)
+    if (!prod_le({M, d_model, 2}, kU32Bytes) || !prod_le({M, N, 2}, kU32Bytes) || !prod_le({d_model, N, 4}, kU32Bytes))
       return fail(GSA_ERR_UNSUPPORTED, "%s: X, dZ or W_theta exceeds 4 GiB", fn);
   }
   const void* ptrs[] = {X, W, G, Q, K, V, Y, dY, dX, dW, dQ, dK, dV, workspace};
@@ -496,10 +512,12 @@ gsa_status gsa_project_qkvg(const void* X, const void* W, void* Q, void* K, void
     return fail(GSA_ERR_INVALID_ARG, "%s: G must be NULL exactly when n_gate is 0", fn);
   if (gsa_status st = check_dtype(fn, dtype)) return st;
   if (dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "%s: only GSA_BF16 is supported", fn);
+  if (Hq > 4096 || D > 4096 || n_gate > kIntMax)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
   const int64_t nq = Hq * D, nkv = Hkv * D, N = nq + 2 * nkv + n_gate;
   if (d_model % 8 != 0 || nq % 8 != 0 || nkv % 8 != 0 || n_gate % 8 != 0)
     return fail(GSA_ERR_UNSUPPORTED, "%s: d_model and every output width must be multiples of 8", fn);
-  if (M * d_model * 2 >= kIntMax || d_model * N * 2 >= kIntMax || M > kIntMax)
+  if (!prod_le({M, d_model, 2}, kIntMax - 1) || !prod_le({d_model, N, 2}, kIntMax - 1))
     return fail(GSA_ERR_UNSUPPORTED, "%s: X or W exceeds 2 GiB", fn);
   if (!aligned16(X) || !aligned16(W) || !aligned16(Q) || !aligned16(K) || !aligned16(V) || (G && !aligned16(G)))
     return fail(GSA_ERR_MISALIGNED, "%s: X, W, Q, K, V and G must be 16-byte aligned", fn);
@@ -543,7 +561,7 @@ gsa_status gsa_value_gate(const void* V, const float* G, void* Vout, int64_t B, 
     return fail(GSA_ERR_INVALID_ARG, "%s: layout must be GSA_GATE_ELEMENTWISE or GSA_GATE_HEADWISE", fn);
   if (gsa_status st = check_dtype(fn, dtype)) return st;
   if (D != 64 && D != 128) return fail(GSA_ERR_UNSUPPORTED, "%s: head dim %lld is not 64 or 128", fn, (long long)D);
-  if (B * S > kIntMax || B * S * Hkv * D > ((int64_t)1 << 40))
+  if (!prod_le({B, S}, kIntMax) || !prod_le({B, S, Hkv, D}, kElemMax))
     return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
   if (!aligned16(V) || !aligned16(G) || !aligned16(Vout))
     return fail(GSA_ERR_MISALIGNED, "%s: V, G and Vout must be 16-byte aligned", fn);
@@ -560,7 +578,7 @@ gsa_status gsa_gate_head_mean(const float* G, float* Gs, int64_t M, int64_t Hq, 
     return fail(GSA_ERR_INVALID_ARG, "%s: sizes must be positive (M=%lld Hq=%lld D=%lld)", fn, (long long)M,
                 (long long)Hq, (long long)D);
   if (D % 4 != 0) return fail(GSA_ERR_UNSUPPORTED, "%s: D=%lld is not a multiple of 4", fn, (long long)D);
-  if (Hq > 4096 || D > 4096 || M > kIntMax || M * Hq * D > ((int64_t)1 << 40))
+  if (Hq > 4096 || D > 4096 || M > kIntMax || !prod_le({M, Hq, D}, kElemMax))
     return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
   if (!aligned16(G) || !aligned16(Gs)) return fail(GSA_ERR_MISALIGNED, "%s: G and Gs must be 16-byte aligned", fn);
   const uintptr_t g0 = (uintptr_t)G, g1 = g0 + (uintptr_t)(M * Hq * D) * 4;
