@@ -73,14 +73,18 @@ __device__ __forceinline__ float variant_combine(float y, float g, const FwdEpi&
 
 #define GSA_LDS __attribute__((address_space(3)))
 
-template <int D, int MODE, int QB>
+// HG > 1 (GQA): the 4 waves take HG query heads of one key/value group, 4/HG
+// row blocks each, so one staged K/V tile serves HG heads (HG times fewer K/V
+// loads per matrix op, and every wave's rows end at the workgroup's diagonal).
+template <int D, int MODE, int QB, int HG = 1>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1)
 void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                           const bf16* __restrict__ V, const float* __restrict__ Gate,
                           bf16* __restrict__ Y, float* __restrict__ Lse, int B, int S, int Hq,
                           int Hkv, int n_qtiles, float scale_log2, FwdEpi ep) {
   using namespace fwd;
-  constexpr int BMQ = BM * QB;    // query rows per workgroup (QB blocks of 32 per wave)
+  static_assert(HG == 1 || (QB == 1 && 4 % HG == 0), "head groups of 2 or 4 with 32-row waves");
+  constexpr int BMQ = BM * QB / HG;   // query rows per workgroup (QB blocks of 32 per wave)
   constexpr int CH = D / 8;       // 16-byte chunks per K/V row
   constexpr int KSL = CH + 1;     // K row stride in 16-B slots (one pad slot: 4-bank rotation per row)
   constexpr int VSL = CH;         // V rows are unpadded, chunk-swizzled
@@ -99,12 +103,12 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int l32 = lane & 31, hl = lane >> 5;
 
   // Heaviest (last) query tiles first.  Workgroup ids are dealt round-robin
-  // over the 8 XCDs; when the (batch, head) pair count allows, XCD x = id % 8
-  // takes the x-th contiguous eighth of the pairs (pair = b*Hq + head, so the
-  // query heads of one GQA group are adjacent), which keeps a key/value head's
-  // tiles in one L2.
+  // over the 8 XCDs; when the (batch, head group) pair count allows, XCD x =
+  // id % 8 takes the x-th contiguous eighth of the pairs (pair = b*(Hq/HG) +
+  // head group, so the query heads of one GQA group are adjacent), which keeps
+  // a key/value head's tiles in one L2.
   const int bid = blockIdx.x;
-  const int hb = Hq * B;
+  const int hb = Hq / HG * B;
   int qt, pair;
   if (hb % 8 == 0) {
     const int pc = hb / 8, j = bid / 8;
@@ -114,12 +118,12 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     qt = n_qtiles - 1 - bid / hb;
     pair = bid % hb;
   }
-  const int head = pair % Hq;
-  const int b = pair / Hq;
-  const int kvh = head / (Hq / Hkv);
+  const int b = pair / (Hq / HG);
+  const int head = (pair % (Hq / HG)) * HG + wave % HG;   // this wave's query head (wave-uniform)
+  const int kvh = head / (Hq / Hkv);                       // the same for the HG heads of the group
 
   const int q0 = qt * BMQ;
-  const int qw0 = q0 + wave * 32 * QB;  // first query row of this wave
+  const int qw0 = q0 + (wave / HG) * 32 * QB;  // first query row of this wave
   int my_q[QB];                         // this lane's query row in each 32-row block
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw0 + 32 * qb + l32;
@@ -737,15 +741,35 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   }
 }
 
+template <int D, int MODE, int QB, int HG>
+static void launch_bf16_hg(const void* Q, const void* K, const void* V, const float* G, void* Y,
+                           float* Lse, int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st,
+                           FwdEpi ep) {
+  const int nq = ceil_div(S, fwd::BM * QB / HG);
+  const int64_t blocks = (int64_t)nq * (Hq / HG) * B;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE, QB, HG>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, Lse, B, S, Hq,
+                     Hkv, nq, scale_log2, ep);
+}
+
+// GQA groups of 4 or more query heads share each staged K/V tile among 4 heads
+// of a workgroup (groups of 2: among 2)
+#ifndef GSA_FWD_HG
+#define GSA_FWD_HG 4
+#endif
 template <int D, int MODE, int QB = GSA_FWD_QB>
 static void launch_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
                         float* Lse, int B, int S, int Hq, int Hkv, float scale_log2, hipStream_t st,
                         FwdEpi ep = FwdEpi{0, 0, 0}) {
-  const int nq = ceil_div(S, fwd::BM * QB);
-  const int64_t blocks = (int64_t)nq * Hq * B;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE, QB>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, G, (bf16*)Y, Lse, B, S, Hq,
-                     Hkv, nq, scale_log2, ep);
+  const int grp = Hq / Hkv;
+  if (QB == 1 && GSA_FWD_HG >= 4 && grp % 4 == 0)
+    launch_bf16_hg<D, MODE, QB, (QB == 1 && GSA_FWD_HG >= 4) ? 4 : 1>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv,
+                                                                        scale_log2, st, ep);
+  else if (QB == 1 && GSA_FWD_HG >= 2 && grp % 2 == 0)
+    launch_bf16_hg<D, MODE, QB, (QB == 1 && GSA_FWD_HG >= 2) ? 2 : 1>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv,
+                                                                        scale_log2, st, ep);
+  else
+    launch_bf16_hg<D, MODE, QB, 1>(Q, K, V, G, Y, Lse, B, S, Hq, Hkv, scale_log2, st, ep);
 }
 
 template <int D, int MODE>
