@@ -220,9 +220,12 @@ def decode_bench(args, torch, gsa, cfg, keep_batches=0):
     ns = gsa.decode_num_splits(cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.D)
     ws = torch.empty(gsa.decode_workspace_bytes(cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.D),
                      dtype=torch.uint8, device="cuda:0")
+    # the gate of B token rows takes the split-K path (gsa_gate_logits_ws)
+    gws = torch.empty(max(16, gsa.gate_logits_workspace_bytes(cfg.B, cfg.d_model, cfg.N)), dtype=torch.uint8,
+                      device="cuda:0")
 
     def step():
-        gsa.gate_logits(X, W, G=G)
+        gsa.gate_logits(X, W, G=G, workspace=gws)
         gsa.decode(Q, K, V, G, cfg.mode, Y=Y, workspace=ws)
 
     def kernel_only():

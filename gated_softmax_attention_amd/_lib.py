@@ -38,6 +38,8 @@ SIGNATURES = {
     "gsa_status_string": (ctypes.c_char_p, [_I]),
     "gsa_last_error_message": (ctypes.c_char_p, []),
     "gsa_gate_logits": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
+    "gsa_gate_logits_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I]),
+    "gsa_gate_logits_ws": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _SZ, _P]),
     "gsa_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_forward_lse": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_decode_num_splits": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),

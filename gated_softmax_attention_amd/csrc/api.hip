@@ -44,6 +44,9 @@ hipError_t launch_value_gate(const void* V, const float* G, void* Vout, int64_t 
                              bool headwise, bool bf16_inputs, hipStream_t st);
 hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
+size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
+                                   int64_t N, int act, hipStream_t stream);
 hipError_t launch_gate_head_mean(const float* G, float* Gs, int64_t M, int Hq, int D, hipStream_t st);
 int bwd_stat_rows(int S);
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
@@ -201,6 +204,34 @@ gsa_status gsa_gate_logits(const void* X, const void* W, float* G, int64_t M, in
   return hip_result(gsa::launch_gate_gemm(X, W, G, M, d_model, N, dtype == GSA_BF16, activation,
                                           (hipStream_t)stream),
                     "gsa_gate_logits launch");
+}
+
+size_t gsa_gate_logits_workspace_bytes(int64_t M, int64_t d_model, int64_t N, int dtype) {
+  if (M <= 0 || d_model <= 0 || N <= 0 || dtype != GSA_BF16 || d_model % 8 != 0) return 0;
+  if (M > kIntMax || d_model > kIntMax || N > kIntMax) return 0;
+  return gsa::gate_splitk_workspace_bytes(M, d_model, N);
+}
+
+gsa_status gsa_gate_logits_ws(const void* X, const void* W, float* G, int64_t M, int64_t d_model, int64_t N,
+                              int dtype, int activation, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gsa_gate_logits_ws";
+  const size_t need = gsa_gate_logits_workspace_bytes(M, d_model, N, dtype);
+  if (need == 0) {   // a shape without the split-K path: exactly gsa_gate_logits
+    gsa_status st = gsa_gate_logits(X, W, G, M, d_model, N, dtype, activation, stream);
+    return st;
+  }
+  if (!X || !W || !G) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (activation < GSA_ACT_IDENTITY || activation > GSA_ACT_SILU)
+    return fail(GSA_ERR_INVALID_ARG, "%s: activation %d is not a gsa_activation", fn, activation);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(X) || !aligned16(W) || !aligned16(G) || !aligned16(workspace))
+    return fail(GSA_ERR_MISALIGNED, "%s: X, W, G and the workspace must be 16-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_gate_gemm_splitk(X, W, G, (float*)workspace, M, d_model, N, activation,
+                                                 (hipStream_t)stream),
+                    fn);
 }
 
 namespace {

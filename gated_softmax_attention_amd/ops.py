@@ -91,10 +91,16 @@ ACTIVATIONS = {"identity": _lib.GSA_ACT_IDENTITY, "sigmoid": _lib.GSA_ACT_SIGMOI
                "ns_sigmoid": _lib.GSA_ACT_NS_SIGMOID, "silu": _lib.GSA_ACT_SILU}
 
 
-def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, stream=None):
+def gate_logits_workspace_bytes(M, d_model, N, dtype=torch.bfloat16):
+    return int(_lib.load().gsa_gate_logits_workspace_bytes(M, d_model, N, _DTYPES[dtype]))
+
+
+def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, workspace=None, stream=None):
     """G = σ(X·W_θ) (or the logits Z when apply_sigmoid is False), float32 [M, N].
     ``activation`` ("identity", "sigmoid", "ns_sigmoid", "silu") overrides
-    apply_sigmoid.
+    apply_sigmoid.  With ``workspace`` (a device tensor of at least
+    gate_logits_workspace_bytes(M, d_model, N) bytes, or True to allocate one)
+    shapes with few rows take the split-K path (gsa_gate_logits_ws).
 
     X: [..., d_model] (leading dims flattened to M rows); W: [d_model, N].
     """
@@ -116,8 +122,19 @@ def gate_logits(X, W, G=None, apply_sigmoid=True, activation=None, stream=None):
         act = ACTIVATIONS[activation]
     else:
         raise ValueError(f"activation must be one of {list(ACTIVATIONS)}")
-    _lib.check(lib.gsa_gate_logits(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N,
-                                   _dtype(X, W), act, _stream(stream)))
+    if workspace is None:
+        _lib.check(lib.gsa_gate_logits(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N,
+                                       _dtype(X, W), act, _stream(stream)))
+        return G
+    need = int(lib.gsa_gate_logits_workspace_bytes(M, dm, N, _dtype(X, W)))
+    if workspace is True:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device) if need else None
+    elif workspace.device != X.device:
+        raise ValueError("the workspace must be on X's device")
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.check(lib.gsa_gate_logits_ws(_dev(X, "X"), _dev(W, "W"), _dev(G, "G"), M, dm, N, _dtype(X, W), act,
+                                      wp, wb, _stream(stream)))
     return G
 
 
@@ -425,7 +442,7 @@ def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, stream=None):
     """The whole decode path: gate projection + sigmoid for the new token, then decode."""
     B, _, Hq, D = Q.shape
     _check_gate_inputs(X, W, B, Hq, D, mode)
-    G = None if mode == "none" else gate_logits(X, W, stream=stream)
+    G = None if mode == "none" else gate_logits(X, W, workspace=True, stream=stream)
     return decode(Q, Kc, Vc, G, mode, num_splits=num_splits, stream=stream)
 
 

@@ -103,6 +103,29 @@ gsa_status gsa_gate_logits(const void* X, const void* W, float* G,
                            int dtype, int activation, void* stream);
 
 /*
+ * Workspace bytes gsa_gate_logits_ws needs for these sizes: nonzero for the
+ * shapes it splits over K (bf16, at most 128 rows, N a multiple of 8 and at
+ * least 64, fewer than 256 output tiles of 64 × 64: e.g. the gate of one
+ * decode step, M = batch), 0 for every other shape.
+ */
+size_t gsa_gate_logits_workspace_bytes(int64_t M, int64_t d_model, int64_t N, int dtype);
+
+/*
+ * gsa_gate_logits with a workspace, for few token rows (decode).  The gate
+ * scores are the same function ("GatedAttention [2025]" §1.2.2 gating
+ * equation), computed by splitting d_model s ways: each part's partial logits
+ * go to the workspace (float32 [s, M, N]) and are added in part order before the
+ * activation, so the result is deterministic.  Arguments as gsa_gate_logits,
+ * plus the workspace (device memory of at least
+ * gsa_gate_logits_workspace_bytes(M, d_model, N, dtype) bytes, 16-byte
+ * aligned, contents on entry irrelevant).  When that size is 0 this call is
+ * gsa_gate_logits and the workspace may be NULL.  Errors: those of
+ * gsa_gate_logits, and a missing or short workspace -> GSA_ERR_WORKSPACE.
+ */
+gsa_status gsa_gate_logits_ws(const void* X, const void* W, float* G, int64_t M, int64_t d_model, int64_t N,
+                              int dtype, int activation, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal gated SDPA forward (prefill): for every batch b, query head h and
  * query row i,  Y'[b,i,h,:] = (Σ_{j<=i} P_ij V[b,j,h/(Hq/Hkv),:]) ⊙ gate,
  * P_i = softmax_j(Q[b,i,h,:]·K[b,j,c,:] / √D) over j <= i (self included).

@@ -370,3 +370,22 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         _lib.load(str(tmp_path / "libgsa.so"))
+
+
+def test_gate_logits_ws_argument_checks(lib):
+    def gw(X=FAKE, G=FAKE, M=64, dm=4096, N=4096, dt=1, act=1, ws=FAKE, wsb=1 << 30):
+        return lib.gsa_gate_logits_ws(X, FAKE, G, M, dm, N, dt, act, ws, wsb, None)
+    need = lib.gsa_gate_logits_workspace_bytes(64, 4096, 4096, 1)
+    assert need == 4 * 64 * 4096 * 4
+    assert lib.gsa_gate_logits_workspace_bytes(64, 4096, 4096, 0) == 0        # float32: one pass
+    assert lib.gsa_gate_logits_workspace_bytes(0, 4096, 4096, 1) == 0
+    assert gw(X=None) == _lib.GSA_ERR_INVALID_ARG
+    assert gw(act=9) == _lib.GSA_ERR_INVALID_ARG
+    assert gw(ws=None) == _lib.GSA_ERR_WORKSPACE
+    assert gw(wsb=need - 1) == _lib.GSA_ERR_WORKSPACE
+    assert gw(ws=MIS) == _lib.GSA_ERR_MISALIGNED
+    # no split-K for this shape: the call is gsa_gate_logits (its checks apply)
+    assert gw(M=8192, dm=60) == _lib.GSA_ERR_UNSUPPORTED
+    if not have_gpu():
+        assert gw() == _lib.GSA_ERR_NO_DEVICE
+        assert gw(M=8192, dm=2048, N=2048, ws=None, wsb=0) == _lib.GSA_ERR_NO_DEVICE

@@ -423,3 +423,58 @@ def test_loader_check_catches_a_partial_last_instruction():
     # rounded up to whole instructions (the backward loader's kBytes), it fits
     check_loader(9, (32 * 17 + 63) // 64 * 64, lambda s: (s // 17, s % 17) if s % 17 < 16 and s // 17 < 32 else None,
                  32, 16)
+
+
+# ------------------------------------------------------------------ gate GEMM, split-K (few rows)
+def test_gate_gemm_splitk():
+    pinned("gate_gemm.hip",
+           "constexpr int BM = 64, BN = 64, BK = 32, NS = 4, WAVES = 4;",
+           "constexpr int XSLOTS = BM * BK / 8, WSLOTS = BK * BN / 8;",
+           "__host__ __device__ constexpr int x_slot(int row, int c) { return row * (BK / 8) + (c ^ ((row >> 2) & 3)); }",
+           "__host__ __device__ constexpr int w_slot(int krow, int c) { return krow * (BN / 8) + (c ^ (4 * ((krow >> 1) & 1))); }",
+           "const int row = sl >> 2, c = (sl & 3) ^ ((row >> 2) & 3);",
+           "const int krow = sl >> 3, wc = (sl & 7) ^ (4 * ((krow >> 1) & 1));",
+           "for (int kk = 0; kk < 2; ++kk) xa[rb][kk] = xs0 + x_slot(rb * 32 + l32, 2 * kk + hl) * 16;",
+           "const int krow = 8 * (g >> 1) + (si >> 2); const int col = nb * 32 + 16 * (g & 1) + 4 * (si & 3); "
+           "wb[nb] = ws0 + (uint32_t)(w_slot(krow, col >> 3) * 16 + (col & 7) * 2);",
+           "const uint32_t ad = wb[nb] + st * (WSLOTS * 16) + 16 * kk * (BN / 8) * 16;",
+           "(ad + 4 * (BN / 8) * 16)",
+           "float* const red = (float*)&Xs[0][0][0];")
+    BM, BN, BK = 64, 64, 32
+    XSLOTS, WSLOTS = BM * BK // 8, BK * BN // 8
+    assert XSLOTS == 4 * 64 and WSLOTS == 4 * 64                 # four instructions each
+    x_slot = lambda r, c: r * (BK // 8) + (c ^ ((r >> 2) & 3))
+    w_slot = lambda r, c: r * (BN // 8) + (c ^ (4 * ((r >> 1) & 1)))
+    xmap = check_loader(4, XSLOTS, lambda s: (s >> 2, (s & 3) ^ ((s >> 2 >> 2) & 3)), BM, BK // 8)
+    wmap = check_loader(4, WSLOTS, lambda s: (s >> 3, (s & 7) ^ (4 * (((s >> 3) >> 1) & 1))), BK, BN // 8)
+    assert all(xmap[(r, c)] == x_slot(r, c) for r in range(BM) for c in range(BK // 8))
+    assert all(wmap[(r, c)] == w_slot(r, c) for r in range(BK) for c in range(BN // 8))
+    worst = 0
+    for rb in range(2):
+        for kk in range(2):
+            addrs = [x_slot(rb * 32 + (l & 31), 2 * kk + (l >> 5)) * 16 for l in range(64)]
+            for g in range(0, 64, 16):
+                worst = max(worst, conflicts(addrs[g:g + 16], 16))
+    assert worst == 1
+    worst16 = worst32 = 0
+    for nb in range(2):
+        for kk in range(2):
+            for half in (0, 4):
+                addrs = []
+                for lane in range(64):
+                    g, si = lane >> 4, lane & 15
+                    krow = 8 * (g >> 1) + (si >> 2)
+                    col = nb * 32 + 16 * (g & 1) + 4 * (si & 3)
+                    base = w_slot(krow, col >> 3) * 16 + (col & 7) * 2
+                    a = base + 16 * kk * (BN // 8) * 16 + half * (BN // 8) * 16
+                    row = krow + half + 16 * kk
+                    assert wmap[(row, col >> 3)] * 16 == a - (col & 7) * 2    # +4 / +16 rows keep the swizzle
+                    assert a + 8 <= WSLOTS * 16
+                    addrs.append(a)
+                for g0 in range(0, 64, 16):
+                    worst16 = max(worst16, conflicts(addrs[g0:g0 + 16], 8))
+                for g0 in range(0, 64, 32):
+                    worst32 = max(worst32, conflicts(addrs[g0:g0 + 32], 8))
+    assert worst16 == 1 and worst32 == 1
+    # the wave-sum staging [4][64][64] float32 fits the X rings (4 waves x 4 stages x 4 KB)
+    assert 4 * 64 * 64 * 4 <= 4 * 4 * XSLOTS * 16
