@@ -374,6 +374,26 @@ def variants_bench(args, torch, gsa, cfg):
     def vstep():
         gsa.value_gate(V, Gv, "elementwise", Vout=Vo)
 
+    # G2 whole steps: the value gate σ(X·W_v) then attention over V ⊙ g, gated as
+    # the forward stages its value tiles, against the separate V' pass
+    Wv = W[:, :Nv].contiguous()
+    Gvs = torch.empty((cfg.B * cfg.S, Nv), dtype=torch.float32, device="cuda:0")
+    Vp = torch.empty_like(V)
+
+    def g2_fused():
+        gsa.gate_logits(X, Wv, G=Gvs)
+        gsa.forward_value_gated(Q, K, V, Gvs, "elementwise", Y=Y)
+
+    def g2_separate():
+        gsa.gate_logits(X, Wv, G=Gvs)
+        gsa.value_gate(V, Gvs, "elementwise", Vout=Vp)
+        gsa.forward(Q, K, Vp, None, "none", Y=Y)
+
+    g2_flops = cfg.attention_flops() + 2 * cfg.B * cfg.S * cfg.d_model * Nv
+    for key, fn in (("g2_value_gate_in_forward", g2_fused), ("g2_value_gate_separate_pass", g2_separate)):
+        m = measure(fn, None, args, torch)
+        out[key] = {"ms_per_step": m["ms"], "median_ms": m["median_ms"], "min_ms": m["min_ms"],
+                    "value": g2_flops / (m["ms"] * 1e-3) / 1e12, "unit": "TFLOP/s", "flops_per_step": g2_flops}
     m = measure(vstep, None, args, torch)
     ms = m["ms"]
     nbytes = 2 * V.numel() * V.element_size() + Gv.numel() * 4

@@ -52,6 +52,7 @@ SIGNATURES = {
     "gsa_forward_variant": (_I, [_P] * 6 + [_I64] * 5 + [_I, _I, _I, _I, _P]),
     "gsa_decode_variant": (_I, [_P] * 5 + [_I64] * 5 + [_I, _I, _I, _I, _I, _P, _SZ, _P]),
     "gsa_gate_head_mean": (_I, [_P, _P, _I64, _I64, _I64, _P]),
+    "gsa_forward_value_gated": (_I, [_P] * 6 + [_I64] * 5 + [_I, _I, _P]),
     "gsa_value_gate": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _I, _I, _P]),
     "gsa_project_qkvg": (_I, [_P] * 6 + [_I64] * 6 + [_I, _P]),
     "gsa_first_token_attention": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),

@@ -47,6 +47,9 @@ hipError_t launch_first_token_share(const void* Q, const void* K, const float* L
 size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
                                    int64_t N, int act, hipStream_t stream);
+hipError_t launch_attn_fwd_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
+                                       float* Lse, int B, int S, int Hq, int Hkv, int D, bool headwise,
+                                       bool bf16_inputs, hipStream_t stream);
 hipError_t launch_gate_head_mean(const float* G, float* Gs, int64_t M, int Hq, int D, hipStream_t st);
 int bwd_stat_rows(int S);
 hipError_t launch_bwd_gemm_dx(const void* dZ, const void* W, void* dX, int64_t M, int64_t d_model,
@@ -580,6 +583,26 @@ gsa_status gsa_forward_variant(const void* Q, const void* K, const void* V, cons
   return hip_result(gsa::launch_attn_fwd_variant(Q, K, V, G, Y, LSE, (int)B, (int)S, (int)Hq, (int)Hkv, (int)D,
                                                  layout, combine == GSA_COMBINE_ADD, norm == GSA_NORM_RMS,
                                                  dtype == GSA_BF16, (hipStream_t)stream),
+                    fn);
+}
+
+gsa_status gsa_forward_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
+                                   float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int layout, int dtype, void* stream) {
+  const char* fn = "gsa_forward_value_gated";
+  if (!Q || !K || !V || !Gv || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (layout != GSA_GATE_ELEMENTWISE && layout != GSA_GATE_HEADWISE)
+    return fail(GSA_ERR_INVALID_ARG, "%s: layout must be GSA_GATE_ELEMENTWISE or GSA_GATE_HEADWISE", fn);
+  // the shape rules of gsa_forward (the value gate is checked like an output gate)
+  if (gsa_status st = check_attn_shape(fn, B, S, Hq, Hkv, D, layout, Gv)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || !aligned16(Gv))
+    return fail(GSA_ERR_MISALIGNED, "%s: Q, K, V, Gv and Y must be 16-byte aligned", fn);
+  if (LSE && ((uintptr_t)LSE % 4) != 0) return fail(GSA_ERR_MISALIGNED, "%s: LSE must be 4-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  return hip_result(gsa::launch_attn_fwd_value_gated(Q, K, V, Gv, Y, LSE, (int)B, (int)S, (int)Hq, (int)Hkv, (int)D,
+                                                     layout == GSA_GATE_HEADWISE, dtype == GSA_BF16,
+                                                     (hipStream_t)stream),
                     fn);
 }
 

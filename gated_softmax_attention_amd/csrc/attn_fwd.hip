@@ -44,7 +44,15 @@ constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 }  // namespace fwd
 
-enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2, kGateVariant = 3 };
+enum : int { kGateNone = 0, kGateElem = 1, kGateHead = 2, kGateVariant = 3, kValueGateElem = 4, kValueGateHead = 5 };
+
+// G2 value gating ("GatedAttention [2025]" §1.2.2, position G2): modes
+// kValueGateElem / kValueGateHead take Gate as σ(X·W_v) per key/value head and
+// dim ([B·S, Hkv·D]) or per key/value head ([B·S, Hkv]) and attend over
+// V' = V ⊙ g, each product rounded once to bf16.  The gate tile of each key
+// tile rides with the V tile's direct loads into LDS, and V' is formed in LDS
+// as soon as the V tile lands, before any PV product reads it; there is no
+// output gate.
 
 // Epilogue of the design-space variants (MODE == kGateVariant only): the gate
 // layout (0 none, 1 elementwise column h·D + d, 2 headwise column h, 3 shared
@@ -96,6 +104,13 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   __shared__ __align__(16) bf16 Ks1[BN * KSL * 8];
   __shared__ __align__(16) bf16 Vs0[BN * VSL * 8];
   __shared__ __align__(16) bf16 Vs1[BN * VSL * 8];
+  // G2 gate tile of the V tile in flight (single-buffered: each one is used up
+  // by the pass over its V tile, behind a barrier, before the next is loaded):
+  // [BN keys][D] float32 elementwise, BN floats headwise (one 4-byte direct
+  // load per lane: 64 slots)
+  constexpr bool kG2 = MODE == kValueGateElem || MODE == kValueGateHead;
+  constexpr int GFL = MODE == kValueGateElem ? BN * D : MODE == kValueGateHead ? 64 : 4;
+  __shared__ __align__(16) float Gst[GFL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -214,6 +229,67 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     for (int j = 0; j < VSL / 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (GSA_LDS void*)&vdst[(wave + 4 * j) * 64 * 8], 16,
                                                (int)(v_off[j] + base), 0, 0, 0);
+  };
+
+  // G2 gate tiles: rows of key tokens k0 .. k0+63 of key/value head kvh; keys
+  // >= S read zeros (range check on the batch's gate rows)
+  const float* const Gv = kG2 ? Gate + ((int64_t)b * S * Hkv + kvh) * (MODE == kValueGateElem ? D : 1) : nullptr;
+  const uint32_t g_row_b = (uint32_t)(Hkv * (MODE == kValueGateElem ? D : 1) * 4);
+  const auto grs = make_rsrc(Gv, kG2 ? (uint32_t)((int64_t)S * g_row_b - (int64_t)kvh * (MODE == kValueGateElem ? D : 1) * 4) : 0u);
+  constexpr int GSL = BN * D / 4;                 // 16-B slots of an elementwise gate tile
+  constexpr int GIW = GSL / 64 / 4;               // its direct loads per wave
+  uint32_t g_off[MODE == kValueGateElem ? GIW : 1];
+  if constexpr (MODE == kValueGateElem) {
+#pragma unroll
+    for (int j = 0; j < GIW; ++j) {
+      const int sl = (wave + 4 * j) * 64 + lane;
+      g_off[j] = (uint32_t)(sl / (D / 4)) * g_row_b + (uint32_t)(sl % (D / 4)) * 16;
+    }
+  } else {
+    g_off[0] = (uint32_t)lane * g_row_b;          // headwise: lane l = key l of the tile
+  }
+  auto dma_g = [&](int k0, bool need) {
+    if constexpr (kG2) {
+      const uint32_t base = need ? (uint32_t)k0 * g_row_b : kNoTile;
+      if constexpr (MODE == kValueGateElem) {
+#pragma unroll
+        for (int j = 0; j < GIW; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (GSA_LDS void*)&Gst[(wave + 4 * j) * 64 * 4], 16,
+                                                   (int)(g_off[j] + base), 0, 0, 0);
+      } else {
+        if (wave == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (GSA_LDS void*)&Gst[0], 4, (int)(g_off[0] + base), 0, 0, 0);
+      }
+    }
+  };
+  // V' = V ⊙ g in place, one RNE rounding per product: thread t takes V slots
+  // t, t + 256, ... (16 bytes: 8 dims of one key; slot phys of row r holds
+  // chunk phys ^ 4·(r & VSW))
+  auto gate_v = [&](bf16* vbuf) {
+    if constexpr (kG2) {
+#pragma unroll
+      for (int i = 0; i < BN * VSL / 256; ++i) {
+        const int sl = tid + 256 * i;
+        const int row = sl / VSL, c = (sl % VSL) ^ (4 * (row & VSW));
+        u32x4 v = *(u32x4*)&vbuf[sl * 8];
+        float g[8];
+        if constexpr (MODE == kValueGateElem) {
+          const f32x4 g0 = *(const f32x4*)&Gst[row * D + c * 8];
+          const f32x4 g1 = *(const f32x4*)&Gst[row * D + c * 8 + 4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] = g0[e];
+            g[4 + e] = g1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) g[e] = Gst[row];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[w] = pack_bf16x2(bf16_lo(v[w]) * g[2 * w], bf16_hi(v[w]) * g[2 * w + 1]);
+        *(u32x4*)&vbuf[sl * 8] = v;
+      }
+    }
   };
 
   // ---- LDS -> MFMA operands
@@ -377,6 +453,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if ((k0 + BN - 1 > qw0) || (k0 + BN > S)) apply_mask(cur, k0);
     dma_k(k0 + 2 * BN, it + 2 < n_kv, k_cur);
     dma_v(k0 + BN, it + 1 < n_kv, v_nxt);
+    dma_g(k0 + BN, it + 1 < n_kv);
     mma_s(k_nxt, nxt);
     const bool move = softmax_max(cur);
     // the Sᵀ(t+1) block: LDS latency is several matrix ops long, so keep 8 K
@@ -407,13 +484,19 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_run[qb] * alpha[qb] + (ps[qb][0] + ps[qb][1]);
     wait_dma_and_sync();
+    if constexpr (kG2) {   // V(t+1) and its gate have landed: form V' before iteration t+1 reads it
+      gate_v(v_nxt);
+      __syncthreads();
+    }
   };
 
   f32x16 sA[2][QB], sB[2][QB];
   dma_k(0, true, Ks0);
   dma_v(0, true, Vs0);
+  dma_g(0, true);
   dma_k(BN, n_kv > 1, Ks1);
   wait_dma_and_sync();
+  gate_v(Vs0);   // G2 only; published by the barrier below, before the first PV product
   mma_s(Ks0, sA);
   __syncthreads();   // K buffer 0 is refilled in the first iteration
   for (int it = 0; it < n_kv; it += 2) {
@@ -672,7 +755,11 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
       const int j = idx / D, d = idx % D;
       const bool ok = k0 + j < Skv;
       Ks[j * LDF + d] = ok ? Kb[(int64_t)(k0 + j) * kv_row + d] : 0.f;
-      Vs[j * LDF + d] = ok ? Vb[(int64_t)(k0 + j) * kv_row + d] : 0.f;
+      float v = ok ? Vb[(int64_t)(k0 + j) * kv_row + d] : 0.f;
+      if constexpr (MODE == kValueGateElem)   // G2: V' = V ⊙ g, one float32 product
+        v *= ok ? Gate[((int64_t)b * Skv + k0 + j) * kv_row + (int64_t)kvh * D + d] : 0.f;
+      if constexpr (MODE == kValueGateHead) v *= ok ? Gate[((int64_t)b * Skv + k0 + j) * Hkv + kvh] : 0.f;
+      Vs[j * LDF + d] = v;
     }
     __syncthreads();
     float t[BNF];
@@ -807,6 +894,32 @@ hipError_t launch_attn_fwd(const void* Q, const void* K, const void* V, const fl
     dispatch_mode<128>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
   else
     dispatch_mode<64>(mode, bf16_inputs, Q, K, V, G, Y, Lse, B, S, Skv, Hq, Hkv, scale_log2, stream);
+  return hipGetLastError();
+}
+
+// G2 value gating (prefill): attention over V ⊙ g, g per key/value head and dim
+// (elementwise) or per key/value head (headwise); no output gate.
+hipError_t launch_attn_fwd_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
+                                       float* Lse, int B, int S, int Hq, int Hkv, int D, bool headwise,
+                                       bool bf16_inputs, hipStream_t stream) {
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  if (bf16_inputs) {
+    if (D == 128) {
+      if (headwise) launch_bf16<128, kValueGateHead>(Q, K, V, Gv, Y, Lse, B, S, Hq, Hkv, scale_log2, stream);
+      else launch_bf16<128, kValueGateElem>(Q, K, V, Gv, Y, Lse, B, S, Hq, Hkv, scale_log2, stream);
+    } else {
+      if (headwise) launch_bf16<64, kValueGateHead>(Q, K, V, Gv, Y, Lse, B, S, Hq, Hkv, scale_log2, stream);
+      else launch_bf16<64, kValueGateElem>(Q, K, V, Gv, Y, Lse, B, S, Hq, Hkv, scale_log2, stream);
+    }
+  } else {
+    if (D == 128) {
+      if (headwise) launch_f32<128, kValueGateHead>(Q, K, V, Gv, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream);
+      else launch_f32<128, kValueGateElem>(Q, K, V, Gv, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream);
+    } else {
+      if (headwise) launch_f32<64, kValueGateHead>(Q, K, V, Gv, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream);
+      else launch_f32<64, kValueGateElem>(Q, K, V, Gv, Y, Lse, B, S, S, Hq, Hkv, scale_log2, stream);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -347,6 +347,30 @@ def decode_variant(Q, Kc, Vc, G, layout, combine="mul", norm=None, num_splits=0,
     return Y
 
 
+def forward_value_gated(Q, K, V, Gv, layout, Y=None, LSE=None, stream=None):
+    """Causal SDPA over the G2-gated values V ⊙ Gv (Gv = σ(X·W_v) per key/value
+    head and dim, [B*S, Hkv*D], or per key/value head, [B*S, Hkv], float32),
+    gated as the kernel stages the value tiles.  Returns Y (and LSE when an LSE
+    tensor is given)."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, S, Hkv, D] matching Q")
+    if layout not in ("elementwise", "headwise"):
+        raise ValueError("the value gate's layout is 'elementwise' or 'headwise'")
+    _same_device(Q, K=K, V=V, LSE=LSE)
+    Gv = _check_gate(Gv, layout, B * S, Hkv, D, Q, name="Gv")
+    Y = _out(Y, Q)
+    if LSE is not None and (LSE.dtype != torch.float32 or LSE.numel() != B * Hq * S):
+        raise ValueError("LSE must be float32 with B*Hq*S elements")
+    lib = _lib.load()
+    _lib.check(lib.gsa_forward_value_gated(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(Gv, "Gv"), _dev(Y, "Y"),
+        None if LSE is None else _dev(LSE, "LSE"), B, S, Hq, Hkv, D, LAYOUTS[layout], _dtype(Q, K, V, Y),
+        _stream(stream)))
+    return Y if LSE is None else (Y, LSE)
+
+
 def value_gate(V, G, layout, Vout=None, stream=None):
     """G2: V ⊙ G per key/value head (elementwise G [B*S, Hkv*D]) or per head
     (headwise G [B*S, Hkv]); returns the gated values, V's shape and dtype."""

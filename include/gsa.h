@@ -300,12 +300,30 @@ gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, con
 gsa_status gsa_gate_head_mean(const float* G, float* Gs, int64_t M, int64_t Hq, int64_t D, void* stream);
 
 /*
- * G2 value gating ("GatedAttention [2025]" §1.2.2, position G2): the gate
- * scales the value map before attention,
+ * Causal SDPA with G2 value gating ("GatedAttention [2025]" §1.2.2, position
+ * G2: the gate on the value map; §1.3.2 Table 1 rows 6 and 11):
+ *   Y[b,i,h,:] = Σ_{j<=i} P_ij · V'[b,j,c,:],   V' = V ⊙ g,  c = h / (Hq/Hkv)
+ * with P the causal softmax of gsa_forward and g = σ(X·W_v) per key/value head
+ * and dim (GSA_GATE_ELEMENTWISE: Gv [B·S, Hkv·D], column c·D + d) or per
+ * key/value head (GSA_GATE_HEADWISE: Gv [B·S, Hkv], column c), float32 from
+ * gsa_gate_logits.  Each product V·g is rounded once to the value dtype,
+ * inside the kernel as the value tiles are staged (V' never reaches HBM); there
+ * is no output gate.
+ *   Q, K, V, Y and the rules as gsa_forward; LSE optional (as gsa_forward_lse,
+ *   NULL skips it).
+ */
+gsa_status gsa_forward_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
+                                   float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int layout, int dtype, void* stream);
+
+/*
+ * G2 value gating as a separate pass ("GatedAttention [2025]" §1.2.2, position
+ * G2): the gate scales the value map before attention,
  *   Vout[t, c, d] = V[t, c, d] · G[t, c*D + d]   (GSA_GATE_ELEMENTWISE)
  *   Vout[t, c, d] = V[t, c, d] · G[t, c]         (GSA_GATE_HEADWISE)
  * for token rows t < B*S and key/value heads c; gsa_forward with mode
- * GSA_GATE_NONE on Vout then gives the G2-gated attention.
+ * GSA_GATE_NONE on Vout then gives the G2-gated attention
+ * (gsa_forward_value_gated does both in one pass, without Vout).
  *   V, Vout : [B, S, Hkv, D] of dtype (may not overlap)   G : float32 from
  *   gsa_gate_logits (σ of X·W_v).  D in {64, 128}; pointers 16-byte aligned.
  */

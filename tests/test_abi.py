@@ -389,3 +389,19 @@ def test_gate_logits_ws_argument_checks(lib):
     if not have_gpu():
         assert gw() == _lib.GSA_ERR_NO_DEVICE
         assert gw(M=8192, dm=2048, N=2048, ws=None, wsb=0) == _lib.GSA_ERR_NO_DEVICE
+
+
+def test_forward_value_gated_argument_checks(lib):
+    def fv(Gv=FAKE, layout=1, D=128, dt=1, Hkv=2, lse=None):
+        return lib.gsa_forward_value_gated(FAKE, FAKE, FAKE, Gv, FAKE, lse, 1, 64, 4, Hkv, D, layout, dt, None)
+    assert fv(Gv=None) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(layout=0) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(layout=3) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(Hkv=3) == _lib.GSA_ERR_INVALID_ARG
+    assert fv(D=96) == _lib.GSA_ERR_UNSUPPORTED
+    assert fv(dt=5) == _lib.GSA_ERR_UNSUPPORTED
+    assert fv(Gv=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert fv(lse=FAKE + 2) == _lib.GSA_ERR_MISALIGNED
+    if not have_gpu():
+        assert fv() == _lib.GSA_ERR_NO_DEVICE
+        assert fv(layout=2, D=64, dt=0, lse=FAKE) == _lib.GSA_ERR_NO_DEVICE

@@ -56,7 +56,7 @@ def test_gate_saturation_and_half_are_exact():
 
 
 # --------------------------------------------------------------- split-K path for few rows
-SPLITK = [(64, 4096, 4096), (1, 512, 64), (37, 1000, 520), (128, 2048, 1024), (64, 4096, 136), (100, 520, 4096)]
+SPLITK = [(64, 4096, 4096), (1, 2048, 64), (37, 2000, 520), (128, 2048, 1024), (64, 4096, 136), (100, 3080, 4096)]
 
 
 @pytest.mark.parametrize("act", ["sigmoid", "identity", "silu"])

@@ -155,6 +155,56 @@ def test_value_gating_g2(layout, dtype):
     report(f64(Y), want, TOL[dtype], f"G2 {dtype} {layout}")
 
 
+def value_gate_inputs(cfg, layout, seed):
+    inp = make_inputs(cfg.with_(mode="none"), seed=seed, device=DEV)
+    N = cfg.Hkv * cfg.D if layout == "elementwise" else cfg.Hkv
+    gx = torch.Generator(device=DEV).manual_seed(seed + 1)
+    Wv = (torch.randn(cfg.d_model, N, generator=gx, device=DEV) / math.sqrt(cfg.d_model)).to(inp["X"].dtype)
+    return inp, Wv, gsa.gate_logits(inp["X"], Wv)
+
+
+G2_CASES = [(2, 257, 8, 2, 128), (1, 200, 4, 4, 64), (1, 64, 8, 1, 128), (2, 1000, 16, 4, 128), (1, 129, 2, 2, 64)]
+
+
+@pytest.mark.parametrize("layout", ["elementwise", "headwise"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,S,Hq,Hkv,D", G2_CASES)
+def test_value_gating_in_the_forward(B, S, Hq, Hkv, D, dtype, layout):
+    """G2 gated as the forward stages its value tiles (gsa_forward_value_gated)
+    against the oracle's SDPA over V ⊙ σ(X·W_v), and bitwise equal to the
+    separate pass (V' = V ⊙ g rounded once, then the ungated forward): the
+    same rounded V' enters the same arithmetic."""
+    cfg = CONFIGS["tiny_fp32"].with_(name="t", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, d_model=64)
+    inp, Wv, Gv = value_gate_inputs(cfg, layout, seed=S + Hq + D)
+    Y, guard = guarded_empty(tuple(inp["Q"].shape), inp["Q"].dtype, DEV)
+    gsa.forward_value_gated(inp["Q"], inp["K"], inp["V"], Gv, layout, Y=Y)
+    Y2 = gsa.forward(inp["Q"], inp["K"], gsa.value_gate(inp["V"], Gv, layout), None, "none")
+    torch.cuda.synchronize()
+    assert guard_ok(guard), "write past the end of Y"
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(Y.view(itype), Y2.view(itype))
+    want = ov.value_gated_sdpa(f64(inp["X"]), f64(Wv), f64(inp["Q"]), f64(inp["K"]), f64(inp["V"]), layout)
+    report(f64(Y), want, TOL[dtype], f"G2 in the forward {dtype} {layout} B{B} S{S} {Hq}/{Hkv} D{D}")
+
+
+@pytest.mark.parametrize("name,layout", [("dense_prefill", "elementwise"), ("gqa_prefill", "headwise")])
+def test_value_gating_in_the_forward_full_size(name, layout):
+    """The dense (B 2, S 4096, 16/16 heads) and GQA (B 1, S 8192, 32/4 heads)
+    prefill shapes with a G2 gate: every output element against the oracle, the
+    LSE against the oracle's, and bitwise equal to the separate pass."""
+    cfg = CONFIGS[name]
+    inp, Wv, Gv = value_gate_inputs(cfg, layout, seed=0)
+    LSE = torch.empty((cfg.B, cfg.Hq, cfg.S), dtype=torch.float32, device=DEV)
+    Y, LSE = gsa.forward_value_gated(inp["Q"], inp["K"], inp["V"], Gv, layout, LSE=LSE)
+    Y2 = gsa.forward(inp["Q"], inp["K"], gsa.value_gate(inp["V"], Gv, layout), None, "none")
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    Vg = ov.value_gate(f64(inp["X"]), f64(Wv), f64(inp["V"]), layout)
+    want, lse = oracle.sdpa(f64(inp["Q"]), f64(inp["K"]), Vg, return_lse=True)
+    report(f64(Y), want, TOL["bf16"], f"{name} G2 {layout} every element")
+    report(LSE.cpu().numpy(), lse, 4e-3, f"{name} G2 LSE")
+
+
 @pytest.mark.parametrize("name,layout,combine,norm", [("dense_prefill", "shared", "add", "rms"),
                                                      ("dense_prefill", "headwise", "mul", "rms"),
                                                      ("gqa_prefill", "shared", "add", "rms"),

@@ -478,3 +478,42 @@ def test_gate_gemm_splitk():
     assert worst16 == 1 and worst32 == 1
     # the wave-sum staging [4][64][64] float32 fits the X rings (4 waves x 4 stages x 4 KB)
     assert 4 * 64 * 64 * 4 <= 4 * 4 * XSLOTS * 16
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_value_gate_tile(D):
+    """G2 in the forward: the gate tile loader (elementwise: 16-byte loads of a
+    64-key x D float32 tile; headwise: one 4-byte load per lane, 64 keys) and
+    the in-place pass, whose thread t takes V slots t, t+256, ... and reads the
+    gates of that slot's 8 dims."""
+    pinned("attn_fwd.hip",
+           "constexpr int GFL = MODE == kValueGateElem ? BN * D : MODE == kValueGateHead ? 64 : 4;",
+           "__shared__ __align__(16) float Gst[GFL];",
+           "constexpr int GSL = BN * D / 4;", "constexpr int GIW = GSL / 64 / 4;",
+           "const int sl = (wave + 4 * j) * 64 + lane; g_off[j] = (uint32_t)(sl / (D / 4)) * g_row_b + (uint32_t)(sl % (D / 4)) * 16;",
+           "(GSA_LDS void*)&Gst[(wave + 4 * j) * 64 * 4], 16,",
+           "g_off[0] = (uint32_t)lane * g_row_b;",
+           "(GSA_LDS void*)&Gst[0], 4,",
+           "for (int i = 0; i < BN * VSL / 256; ++i) { const int sl = tid + 256 * i; "
+           "const int row = sl / VSL, c = (sl % VSL) ^ (4 * (row & VSW));",
+           "const f32x4 g0 = *(const f32x4*)&Gst[row * D + c * 8];")
+    BN, CH = 64, D // 8
+    VSL, VSW = CH, CH // 4 - 1
+    GSL = BN * D // 4
+    GIW = GSL // 64 // 4
+    assert GIW * 4 * 64 == GSL                           # whole instructions fill the tile exactly
+    gmap = check_loader(GSL // 64, GSL, lambda s: (s // (D // 4), s % (D // 4)), BN, D // 4)
+    # headwise: 64 lanes x 4 bytes = 64 floats, the buffer's size
+    assert 64 * 4 <= 64 * 4
+    # the pass covers every V slot once and reads the gate slots of its 8 dims
+    vmap = {(s // VSL, (s % VSL) ^ (4 * ((s // VSL) & VSW))): s for s in range(BN * VSL)}
+    seen = set()
+    for tid in range(256):
+        for i in range(BN * VSL // 256):
+            sl = tid + 256 * i
+            row, c = sl // VSL, (sl % VSL) ^ (4 * ((sl // VSL) & VSW))
+            assert vmap[(row, c)] == sl
+            seen.add(sl)
+            for half in range(2):             # floats row*D + 8c .. +7 = gate slots 2c, 2c + 1 of the row
+                assert gmap[(row, 2 * c + half)] * 4 == row * D + c * 8 + 4 * half
+    assert seen == set(range(BN * VSL))
