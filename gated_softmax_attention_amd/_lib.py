@@ -47,6 +47,8 @@ SIGNATURES = {
     "gsa_decode": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
     "gsa_noalloc_scratch_bytes": (_SZ, []),
     "gsa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _P]),
+    "gsa_gated_decode_workspace_bytes": (_SZ, [_I64] * 6 + [_I, _I, _I]),
+    "gsa_gated_decode": (_I, [_P] * 6 + [_I64] * 6 + [_I, _I, _I, _P, _SZ, _P]),
     "gsa_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _I64, _I]),
     "gsa_backward": (_I, [_P] * 14 + [_I64] * 6 + [_I, _I, _P, _SZ, _P]),
     "gsa_forward_variant": (_I, [_P] * 6 + [_I64] * 5 + [_I, _I, _I, _I, _P]),

@@ -45,6 +45,10 @@ hipError_t launch_value_gate(const void* V, const float* G, void* Vout, int64_t 
 hipError_t launch_first_token_share(const void* Q, const void* K, const float* Lse, float* F, float* head_mean,
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int64_t gate_splitk_splits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gated_decode_bf16(const void* X, const void* W, const void* Q, const void* K, const void* V,
+                                    void* Y, void* workspace, float* gate_part, int B, int L, int Hq, int Hkv,
+                                    int d_model, int nsplit, hipStream_t st);
 hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
                                    int64_t N, int act, hipStream_t stream);
 hipError_t launch_attn_fwd_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
@@ -391,6 +395,93 @@ gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, con
   return hip_result(gsa::launch_decode_bf16(Q, Kc, Vc, G, Y, ws, (int)B, (int)L, (int)Hq, (int)Hkv, (int)D, mode,
                                             (int)ns, (hipStream_t)stream),
                     fn);
+}
+
+namespace {
+// gsa_gated_decode's plan: whether the gate is folded into the decode launches
+// (bf16, D = 128, elementwise, and the split-K gate applies), and its workspace layout
+// [decode partials | gate area], the gate area holding the gate parts
+// (folded) or G (otherwise), each 256-byte aligned.
+struct GatedDecodePlan {
+  bool fused = false;
+  int64_t ns = 0;
+  size_t dec_bytes = 0, gate_off = 0, total = 0;
+};
+GatedDecodePlan gated_decode_plan(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model,
+                                  int mode, int dtype, int num_splits) {
+  GatedDecodePlan p;
+  if (dtype == GSA_BF16) {
+    p.ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+    p.dec_bytes = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
+  }
+  const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
+  size_t gate_bytes = 0;
+  if (mode != GSA_GATE_NONE) {
+    const int64_t gs = dtype == GSA_BF16 && mode == GSA_GATE_ELEMENTWISE && D == 128 && d_model % 8 == 0
+                           ? gsa::gate_splitk_splits(B, d_model, N) : 0;
+    p.fused = gs > 0;
+    gate_bytes = (size_t)((p.fused ? gs : 1) * B * N) * sizeof(float);
+  }
+  p.gate_off = (p.dec_bytes + 255) & ~(size_t)255;
+  p.total = p.gate_off + gate_bytes;
+  return p;
+}
+}  // namespace
+
+size_t gsa_gated_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model,
+                                        int mode, int dtype, int num_splits) {
+  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || num_splits < 0) return 0;
+  if (mode != GSA_GATE_NONE && mode != GSA_GATE_ELEMENTWISE && mode != GSA_GATE_HEADWISE) return 0;
+  if (mode != GSA_GATE_NONE && (d_model <= 0 || d_model > kIntMax)) return 0;
+  if (!prod_le({B, L}, kIntMax) || Hq > 4096 || D > 4096) return 0;
+  if (mode != GSA_GATE_NONE && (!prod_le({B, Hq, D, 16}, kElemMax) || !prod_le({B, d_model}, kElemMax) ||
+                                 !prod_le({d_model, Hq, D}, kElemMax)))
+    return 0;
+  return gated_decode_plan(B, L, Hq, Hkv, D, d_model, mode, dtype, num_splits).total;
+}
+
+gsa_status gsa_gated_decode(const void* X, const void* W, const void* Q, const void* Kc, const void* Vc, void* Y,
+                            int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model, int mode,
+                            int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gsa_gated_decode";
+  const bool gated = mode != GSA_GATE_NONE;
+  if (!Q || !Kc || !Vc || !Y) return fail(GSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (gated != (X != nullptr) || gated != (W != nullptr))
+    return fail(GSA_ERR_INVALID_ARG, "%s: X and W must be given exactly when a gate is", fn);
+  // the shape rules of gsa_decode (checked with a stand-in gate pointer)
+  if (gsa_status st = check_attn_shape(fn, B, L, Hq, Hkv, D, mode, gated ? (const float*)W : nullptr, 1)) return st;
+  if (gsa_status st = check_dtype(fn, dtype)) return st;
+  if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  if (gated && (d_model <= 0 || d_model > kIntMax))
+    return fail(GSA_ERR_INVALID_ARG, "%s: d_model=%lld must be positive", fn, (long long)d_model);
+  if (gated && d_model % 8 != 0)
+    return fail(GSA_ERR_UNSUPPORTED, "%s: d_model=%lld is not a multiple of 8", fn, (long long)d_model);
+  if (gated && (!prod_le({B, Hq, D, 16}, kElemMax) || !prod_le({B, d_model}, kElemMax) ||
+                !prod_le({d_model, Hq, D}, kElemMax)))
+    return fail(GSA_ERR_UNSUPPORTED, "%s: sizes exceed the supported range", fn);
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Y) || (X && !aligned16(X)) ||
+      (W && !aligned16(W)))
+    return fail(GSA_ERR_MISALIGNED, "%s: X, W, Q, Kc, Vc and Y must be 16-byte aligned", fn);
+  const GatedDecodePlan plan = gated_decode_plan(B, L, Hq, Hkv, D, d_model, mode, dtype, num_splits);
+  if (plan.total > 0 && (workspace == nullptr || workspace_bytes < plan.total))
+    return fail(GSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(GSA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+  if (gsa_status st = check_device()) return st;
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  if (plan.fused)
+    return hip_result(gsa::launch_gated_decode_bf16(X, W, Q, Kc, Vc, Y, ws, (float*)(ws + plan.gate_off), (int)B,
+                                                    (int)L, (int)Hq, (int)Hkv, (int)d_model, (int)plan.ns, st),
+                      fn);
+  // otherwise: the gate into the workspace, then the decode
+  float* G = gated ? (float*)(ws + plan.gate_off) : nullptr;
+  if (gated) {
+    const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
+    gsa_status s1 = gsa_gate_logits(X, W, G, B, d_model, N, dtype, GSA_ACT_SIGMOID, stream);
+    if (s1 != GSA_OK) return s1;
+  }
+  return gsa_decode(Q, Kc, Vc, G, Y, B, L, Hq, Hkv, D, mode, dtype, num_splits, ws, plan.dec_bytes, stream);
 }
 
 gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, const float* G, void* Y, int64_t B,

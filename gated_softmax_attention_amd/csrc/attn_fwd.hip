@@ -79,7 +79,6 @@ __device__ __forceinline__ float variant_combine(float y, float g, const FwdEpi&
 #define GSA_FWD_QB 1
 #endif
 
-#define GSA_LDS __attribute__((address_space(3)))
 
 // HG > 1 (GQA): the 4 waves take HG query heads of one key/value group, 4/HG
 // row blocks each, so one staged K/V tile serves HG heads (HG times fewer K/V

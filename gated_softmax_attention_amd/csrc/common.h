@@ -8,6 +8,9 @@
 #include <type_traits>
 #include <utility>
 
+// pointer qualifier for LDS (local data share) addresses
+#define GSA_LDS __attribute__((address_space(3)))
+
 namespace gsa {
 
 typedef __bf16 bf16;

@@ -462,12 +462,41 @@ def gated_attention(X, W, Q, K, V, mode, stream=None):
     return forward(Q, K, V, G, mode, stream=stream)
 
 
-def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, stream=None):
-    """The whole decode path: gate projection + sigmoid for the new token, then decode."""
-    B, _, Hq, D = Q.shape
+def gated_decode_workspace_bytes(B, L, Hq, Hkv, D, d_model, mode, dtype=torch.bfloat16, num_splits=0):
+    return int(_lib.load().gsa_gated_decode_workspace_bytes(B, L, Hq, Hkv, D, d_model, _mode(mode), _DTYPES[dtype],
+                                                             num_splits))
+
+
+def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, Y=None, workspace=None, stream=None):
+    """The whole decode path in one call (gsa_gated_decode): the gate σ(X·W_θ) of
+    the B new tokens and the decode of Q [B,1,Hq,D] against Kc/Vc [B,L,Hkv,D];
+    with bf16, D 128 and the elementwise gate, the gate is folded into the
+    decode's launches."""
+    B, one, Hq, D = Q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per batch")
+    L, Hkv = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, L, Hkv, D) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B, L, Hkv, D] matching Q")
     _check_gate_inputs(X, W, B, Hq, D, mode)
-    G = None if mode == "none" else gate_logits(X, W, workspace=True, stream=stream)
-    return decode(Q, Kc, Vc, G, mode, num_splits=num_splits, stream=stream)
+    gated = _mode(mode) != _lib.GSA_GATE_NONE
+    if not gated and (X is not None or W is not None):
+        raise ValueError("X and W must be None without a gate")
+    _same_device(Q, Kc=Kc, Vc=Vc, X=X, W=W, workspace=workspace)
+    if gated:
+        _dtype(Q, Kc, Vc, X, W)
+    Y = _out(Y, Q)
+    dm = X.shape[-1] if gated else 0
+    need = gated_decode_workspace_bytes(B, L, Hq, Hkv, D, dm, mode, Q.dtype, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gsa_gated_decode(None if X is None else _dev(X, "X"), None if W is None else _dev(W, "W"),
+                                    _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), _dev(Y, "Y"), B, L, Hq, Hkv, D, dm,
+                                    _mode(mode), _dtype(Q, Kc, Vc, Y), num_splits, wp, wb, _stream(stream)))
+    return Y
 
 
 def gated_attention_variant(X, W, Q, K, V, layout, activation="sigmoid", combine="mul", norm=None, stream=None):

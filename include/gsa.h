@@ -211,6 +211,34 @@ gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, con
                               int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
                               int mode, int dtype, int num_splits, void* stream);
 
+/* Workspace bytes gsa_gated_decode needs for these sizes (0 for invalid sizes). */
+size_t gsa_gated_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model,
+                                        int mode, int dtype, int num_splits);
+
+/*
+ * The whole decode step in one call: the gate scores of the B new tokens,
+ * σ(X·W_θ) ("GatedAttention [2025]" §1.2.2 gating equation), and the gated
+ * decode of gsa_decode (the KV cache of §1.3.1), i.e. gsa_gate_logits then
+ * gsa_decode.
+ *   X : [B, d_model] (the new tokens' hidden states), W : [d_model, N] (dtype),
+ *       N = Hq·D (ELEMENTWISE) or Hq (HEADWISE); both NULL for GSA_GATE_NONE.
+ *   Q, Kc, Vc, Y, num_splits: as gsa_decode.
+ *   workspace: at least gsa_gated_decode_workspace_bytes(...) bytes, 16-byte
+ *     aligned, contents on entry irrelevant.
+ * For bf16, D = 128 and the elementwise gate, when the split-K gate of
+ * gsa_gate_logits_ws applies to [B, d_model]·[d_model, Hq·D], the gate is
+ * folded into the decode's two launches: the split kernel's grid starts with
+ * the split-K gate workgroups (64×64 tiles of X·W_θ over parts of d_model),
+ * and the merge adds the parts in order and applies σ; Y then equals
+ * gsa_gate_logits_ws followed by gsa_decode bit for bit.  Other cases run
+ * gsa_gate_logits and gsa_decode.
+ * Errors: those of gsa_gate_logits and gsa_decode; X and W given without a
+ * gate (or missing with one) -> GSA_ERR_INVALID_ARG.
+ */
+gsa_status gsa_gated_decode(const void* X, const void* W, const void* Q, const void* Kc, const void* Vc, void* Y,
+                            int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model, int mode,
+                            int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Workspace bytes gsa_backward needs for these sizes (0 for invalid sizes;
  * d_model is ignored for GSA_GATE_NONE).

@@ -85,6 +85,21 @@ int main() {
   expect("noalloc big", gsa_decode_noalloc(P, P, P, F, P, 64, 16384, 32, 8, 128, 1, 1, 8, nullptr), {WS});
   expect("noalloc huge", gsa_decode_noalloc(P, P, P, F, P, BIG, BIG, 32, 8, 128, 1, 1, 0, nullptr), {UNS});
   VALID("noalloc ok", gsa_decode_noalloc(P, P, P, F, P, 64, 16384, 32, 8, 128, 1, 1, 0, nullptr));
+  expect("gdec ws huge", gsa_gated_decode_workspace_bytes(BIG, BIG, BIG, 1, 128, BIG, 1, 1, 0) >= 0, {1});
+  expect("gdec ws huge2", gsa_gated_decode_workspace_bytes(HUGE2, 2, 4096, 1, 4096, HUGE2, 1, 1, 0) == 0, {1});
+  const size_t gws = gsa_gated_decode_workspace_bytes(64, 16384, 32, 8, 128, 4096, 1, 1, 0);
+  expect("gdec ws", gws > 0, {1});
+  expect("gdec null", gsa_gated_decode(nullptr, P, P, P, P, P, 64, 16384, 32, 8, 128, 4096, 1, 1, 0, P2, gws,
+                                       nullptr), {INV});
+  expect("gdec ws small", gsa_gated_decode(P, P, P, P, P, P, 64, 16384, 32, 8, 128, 4096, 1, 1, 0, P2, 16,
+                                           nullptr), {WS});
+  expect("gdec huge", gsa_gated_decode(P, P, P, P, P, P, BIG, BIG, 32, 8, 128, 4096, 1, 1, 0, P2, gws, nullptr),
+         {UNS});
+  expect("gdec huge dm", gsa_gated_decode(P, P, P, P, P, P, 64, 16, 32, 8, 128, HUGE2, 1, 1, 0, P2, gws, nullptr),
+         {UNS, INV});
+  VALID("gdec ok", gsa_gated_decode(P, P, P, P, P, P, 64, 16384, 32, 8, 128, 4096, 1, 1, 0, P2, gws, nullptr));
+  VALID("gdec none", gsa_gated_decode(nullptr, nullptr, P, P, P, P, 2, 100, 8, 2, 128, 0, 0, 1, 0, P2, 1 << 30,
+                                      nullptr));
   expect("dvar layout", gsa_decode_variant(P, P, P, F, P, 2, 100, 8, 2, 128, 5, 0, 0, 1, 0, P2, 1 << 30, nullptr),
          {INV});
   VALID("dvar ok", gsa_decode_variant(P, P, P, F, P, 2, 100, 8, 2, 128, 3, 1, 1, 1, 0, P2, 1 << 30, nullptr));

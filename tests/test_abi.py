@@ -405,3 +405,36 @@ def test_forward_value_gated_argument_checks(lib):
     if not have_gpu():
         assert fv() == _lib.GSA_ERR_NO_DEVICE
         assert fv(layout=2, D=64, dt=0, lse=FAKE) == _lib.GSA_ERR_NO_DEVICE
+
+
+def test_gated_decode_argument_checks(lib):
+    def gd(X=FAKE, W=FAKE, Q=FAKE, mode=1, D=128, dt=1, dm=4096, ns=0, ws=FAKE, wsb=1 << 30, B=64, L=16384):
+        return lib.gsa_gated_decode(X, W, Q, FAKE, FAKE, FAKE, B, L, 32, 8, D, dm, mode, dt, ns, ws, wsb, None)
+    ws = lambda **k: lib.gsa_gated_decode_workspace_bytes(
+        k.get("B", 64), k.get("L", 16384), 32, 8, k.get("D", 128), k.get("dm", 4096), k.get("mode", 1),
+        k.get("dt", 1), 0)
+    dec = lib.gsa_decode_workspace_bytes(64, 16384, 32, 8, 128, 0)
+    base = (dec + 255) // 256 * 256
+    # folded gate: the split-K gate parts (4 parts of 64 x 4096 floats) after the decode partials
+    assert ws() == base + 4 * 64 * 4096 * 4
+    # headwise, float32: one G after the decode partials (float32 decode has none)
+    assert ws(mode=2) == base + 64 * 32 * 4
+    assert ws(dt=0) == 64 * 4096 * 4
+    assert ws(mode=0) == dec
+    assert ws(mode=7) == 0 and ws(B=0) == 0
+    assert gd(X=None) == _lib.GSA_ERR_INVALID_ARG
+    assert gd(mode=0) == _lib.GSA_ERR_INVALID_ARG              # X and W given without a gate
+    assert gd(Q=None) == _lib.GSA_ERR_INVALID_ARG
+    assert gd(ns=-1) == _lib.GSA_ERR_INVALID_ARG
+    assert gd(dm=0) == _lib.GSA_ERR_INVALID_ARG
+    assert gd(dm=4100) == _lib.GSA_ERR_UNSUPPORTED
+    assert gd(dm=1 << 40) == _lib.GSA_ERR_INVALID_ARG
+    assert gd(D=96) == _lib.GSA_ERR_UNSUPPORTED
+    assert gd(ws=None) == _lib.GSA_ERR_WORKSPACE
+    assert gd(wsb=ws() - 1) == _lib.GSA_ERR_WORKSPACE
+    assert gd(ws=MIS) == _lib.GSA_ERR_MISALIGNED
+    assert gd(X=MIS) == _lib.GSA_ERR_MISALIGNED
+    if not have_gpu():
+        assert gd() == _lib.GSA_ERR_NO_DEVICE
+        assert gd(X=None, W=None, mode=0) == _lib.GSA_ERR_NO_DEVICE
+        assert gd(mode=2, D=64, dt=0, B=2, L=100) == _lib.GSA_ERR_NO_DEVICE

@@ -102,3 +102,39 @@ def test_decode_long_cache():
     inp = make_inputs(cfg, seed=9, device=DEV)
     Y, _ = run(inp, "elementwise")
     report(f64(Y), oracle_decode(inp, "elementwise"), TOL["bf16"], "decode L=262144")
+
+
+# --------------------------------------------------------------- the whole decode step in one call
+@pytest.mark.parametrize("B,L,Hq,Hkv,D,mode,dtype,dm", [
+    (64, 16384, 32, 8, 128, "elementwise", "bf16", 4096),   # the decode workload: gate folded in
+    (8, 3000, 16, 2, 128, "elementwise", "bf16", 2048),     # folded, fewer batches
+    (3, 777, 8, 2, 128, "elementwise", "bf16", 1096),       # ragged d_model tile
+    (4, 1000, 8, 2, 128, "headwise", "bf16", 2048),         # two calls (headwise gate)
+    (2, 500, 8, 2, 64, "elementwise", "bf16", 2048),        # two calls (D 64)
+    (2, 300, 4, 2, 128, "elementwise", "fp32", 256),        # two calls (float32)
+    (2, 300, 4, 2, 128, "none", "bf16", 64),
+])
+def test_gated_decode_one_call(B, L, Hq, Hkv, D, mode, dtype, dm):
+    """gsa_gated_decode against the two calls it stands for (gate, then decode)
+    and against the oracle, every batch.  When the gate is folded into the
+    decode's launches its parts are summed in the same order as the split-K
+    gate's, so the two agree bitwise."""
+    cfg = dec_cfg(B, L, Hq, Hkv, D, mode, dtype, dm=dm)
+    print(f"  gated decode B{B} L{L} {Hq}/{Hkv}x{D} {mode} {dtype} dm{dm}", flush=True)
+    if (B, L) in ((64, 16384), (8, 3000)):
+        # the gate is folded in: the workspace holds the split-K gate parts, not one G
+        dws = gsa.decode_workspace_bytes(B, L, Hq, Hkv, D)
+        gate_area = gsa.gated_decode_workspace_bytes(B, L, Hq, Hkv, D, dm, mode) - (dws + 255) // 256 * 256
+        assert gate_area > B * Hq * D * 4
+    inp = make_inputs(cfg, seed=B + L, device=DEV)
+    X = None if mode == "none" else inp["X"].reshape(B, dm)
+    W = None if mode == "none" else inp["W"]
+    Y, guard = guarded_empty(tuple(inp["Q"].shape), inp["Q"].dtype, DEV)
+    gsa.gated_decode(X, W, inp["Q"], inp["K"], inp["V"], mode, Y=Y)
+    G = None if mode == "none" else gsa.gate_logits(X, W, workspace=True)
+    Y2 = gsa.decode(inp["Q"], inp["K"], inp["V"], G, mode)
+    torch.cuda.synchronize()
+    assert guard_ok(guard), "write past the end of Y"
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(Y.view(itype), Y2.view(itype))
+    report(f64(Y), oracle_decode_by_batch(inp, mode), TOL[dtype], f"gated decode {mode} {dtype} B{B} L{L}")

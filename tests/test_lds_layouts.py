@@ -30,8 +30,13 @@ CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 
 
 def src(name):
-    with open(os.path.join(CSRC, name)) as f:
-        return " ".join(f.read().split())
+    """The source text (whitespace-normalised) of a kernel file and the csrc
+    headers it includes."""
+    text = ""
+    for f in [name] + sorted(h for h in os.listdir(CSRC) if h.endswith(".h")):
+        with open(os.path.join(CSRC, f)) as fh:
+            text += fh.read() + "\n"
+    return " ".join(text.split())
 
 
 def pinned(name, *snippets):
@@ -154,8 +159,8 @@ def test_decode_ring(D):
     pinned("attn_decode.hip",
            "constexpr int KB = 16;", "constexpr int WAVES = 4;", "constexpr int TK = KB * WAVES;",
            "constexpr int NS = 4;",
-           "constexpr int CHK = D / 8;", "constexpr int STG = TK * D;",
-           "__shared__ __align__(16) bf16 Ks[NS][STG];",
+           "constexpr int CHK = D / 8;",
+           "bf16 Ks[dec::NS][dec::TK * D];", "auto& Ks = sm.Ks;",
            "constexpr int NI = TK * CHK / 64 / WAVES;",
            "const int sl = (wave + WAVES * i) * 64 + lane; const int row = sl / CHK, phys = sl % CHK; "
            "dma_off[i] = (uint32_t)row * row_b + (uint32_t)((phys ^ (row & (CHK - 1))) * 16);",
