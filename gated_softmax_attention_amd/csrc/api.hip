@@ -46,9 +46,6 @@ hipError_t launch_first_token_share(const void* Q, const void* K, const float* L
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int64_t gate_splitk_splits(int64_t M, int64_t K, int64_t N);
-hipError_t launch_gated_decode_bf16(const void* X, const void* W, const void* Q, const void* K, const void* V,
-                                    void* Y, void* workspace, float* gate_part, int B, int L, int Hq, int Hkv,
-                                    int d_model, int nsplit, hipStream_t st);
 hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
                                    int64_t N, int act, hipStream_t stream);
 hipError_t launch_attn_fwd_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
@@ -398,32 +395,26 @@ gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, con
 }
 
 namespace {
-// gsa_gated_decode's plan: whether the gate is folded into the decode launches
-// (bf16, D = 128, elementwise, and the split-K gate applies), and its workspace layout
-// [decode partials | gate area], the gate area holding the gate parts
-// (folded) or G (otherwise), each 256-byte aligned.
+// gsa_gated_decode's workspace: [decode partials | split-K gate parts | G],
+// each 256-byte aligned (the gate parts only when gsa_gate_logits_ws takes its
+// split-K path).
 struct GatedDecodePlan {
-  bool fused = false;
-  int64_t ns = 0;
-  size_t dec_bytes = 0, gate_off = 0, total = 0;
+  size_t dec_bytes = 0, gws_off = 0, gws_bytes = 0, g_off = 0, total = 0;
 };
 GatedDecodePlan gated_decode_plan(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model,
                                   int mode, int dtype, int num_splits) {
   GatedDecodePlan p;
-  if (dtype == GSA_BF16) {
-    p.ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
-    p.dec_bytes = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
-  }
-  const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
-  size_t gate_bytes = 0;
+  if (dtype == GSA_BF16) p.dec_bytes = gsa_decode_workspace_bytes(B, L, Hq, Hkv, D, num_splits);
+  size_t off = (p.dec_bytes + 255) & ~(size_t)255;
   if (mode != GSA_GATE_NONE) {
-    const int64_t gs = dtype == GSA_BF16 && mode == GSA_GATE_ELEMENTWISE && D == 128 && d_model % 8 == 0
-                           ? gsa::gate_splitk_splits(B, d_model, N) : 0;
-    p.fused = gs > 0;
-    gate_bytes = (size_t)((p.fused ? gs : 1) * B * N) * sizeof(float);
+    const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
+    p.gws_off = off;
+    p.gws_bytes = gsa_gate_logits_workspace_bytes(B, d_model, N, dtype);
+    off += (p.gws_bytes + 255) & ~(size_t)255;
+    p.g_off = off;
+    off += (size_t)(B * N) * sizeof(float);
   }
-  p.gate_off = (p.dec_bytes + 255) & ~(size_t)255;
-  p.total = p.gate_off + gate_bytes;
+  p.total = off;
   return p;
 }
 }  // namespace
@@ -468,17 +459,13 @@ gsa_status gsa_gated_decode(const void* X, const void* W, const void* Q, const v
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GSA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
   if (gsa_status st = check_device()) return st;
+  // the gate into the workspace (split-K for few rows), then the decode
   char* ws = (char*)workspace;
-  hipStream_t st = (hipStream_t)stream;
-  if (plan.fused)
-    return hip_result(gsa::launch_gated_decode_bf16(X, W, Q, Kc, Vc, Y, ws, (float*)(ws + plan.gate_off), (int)B,
-                                                    (int)L, (int)Hq, (int)Hkv, (int)d_model, (int)plan.ns, st),
-                      fn);
-  // otherwise: the gate into the workspace, then the decode
-  float* G = gated ? (float*)(ws + plan.gate_off) : nullptr;
+  float* G = gated ? (float*)(ws + plan.g_off) : nullptr;
   if (gated) {
     const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;
-    gsa_status s1 = gsa_gate_logits(X, W, G, B, d_model, N, dtype, GSA_ACT_SIGMOID, stream);
+    gsa_status s1 = gsa_gate_logits_ws(X, W, G, B, d_model, N, dtype, GSA_ACT_SIGMOID,
+                                       plan.gws_bytes > 0 ? ws + plan.gws_off : nullptr, plan.gws_bytes, stream);
     if (s1 != GSA_OK) return s1;
   }
   return gsa_decode(Q, Kc, Vc, G, Y, B, L, Hq, Hkv, D, mode, dtype, num_splits, ws, plan.dec_bytes, stream);

@@ -25,7 +25,6 @@
 // splits exactly: m* = max m_s, l* = Σ l_s 2^{m_s − m*}, O* = Σ O_s 2^{m_s − m*},
 // then O*/l* times the gate, rounded once to bf16.
 #include "common.h"
-#include "gate_splitk.h"
 
 namespace gsa {
 
@@ -69,8 +68,7 @@ struct DecSmem {
   float sm_o[dec::WAVES][4][D];
 };
 
-// The split workgroup (split s, key/value head and quad yq, batch b) on the LDS
-// sm; shared by the split kernel and the split kernel with the gate folded in.
+// The split workgroup (split s, key/value head and quad yq, batch b) on the LDS sm.
 template <int D>
 __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
@@ -151,8 +149,8 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t ins = (uint32_t)(wave + WAVES * i) * 64 * 16;
-      dma16_lds(krs, dma_off[i] + base, kd + ins);
-      dma16_lds(vrs, dma_off[i] + base, vd + ins);
+      dma16_lds_nt(krs, dma_off[i] + base, kd + ins);   // the cache is read once: streaming policy
+      dma16_lds_nt(vrs, dma_off[i] + base, vd + ins);
     }
   };
   // wait until at most n stages of this wave's loads are still in flight
@@ -278,53 +276,6 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
   __shared__ __align__(16) DecSmem<D> sm;
   decode_split_body<D>(sm, Q, Kc, Vc, part, L, Hq, Hkv, nsplit, chunk, scale_log2, blockIdx.x, blockIdx.y,
                        blockIdx.z);
-}
-
-// The split kernel with the decode gate folded in: the split-K gate
-// workgroups (64×64 tiles of X·W_θ over d_model parts, gate_splitk.h) lead the
-// grid and run on the same LDS (the K and V rings, 64 KB each at D = 128), so
-// the gate costs no launches of its own; the merge adds the gate parts in part
-// order and applies σ (decode_merge_gatesum_bf16_kernel).
-__global__ __launch_bounds__(256)
-void decode_split_gate_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc,
-                                   const bf16* __restrict__ Vc, float* __restrict__ part, int L, int Hq,
-                                   int Hkv, int nsplit, int chunk, float scale_log2, int ny,
-                                   const bf16* __restrict__ X, const bf16* __restrict__ W,
-                                   float* __restrict__ gate_part, int M, int K, int N, int tiles_n, int gsplits,
-                                   int nk_split, int n_gate) {
-  __shared__ __align__(16) DecSmem<128> sm;
-  static_assert(sizeof(sm.Ks) == 65536 && sizeof(sm.Vs) == 65536, "the gate rings need two 64 KB areas");
-  const int bid = blockIdx.x;
-  if (bid < n_gate) {
-    gate_splitk_body(&sm.Ks[0][0], &sm.Vs[0][0], X, W, gate_part, M, K, N, tiles_n, gsplits, nk_split, bid);
-    return;
-  }
-  const int d = bid - n_gate;
-  decode_split_body<128>(sm, Q, Kc, Vc, part, L, Hq, Hkv, nsplit, chunk, scale_log2, d % nsplit,
-                         (d / nsplit) % ny, d / (nsplit * ny));
-}
-
-// The merge for the folded gate: O*/l* · σ(Σ_s gate_part[s]) (parts added in
-// order, elementwise gate column h·D + d), rounded once.
-template <int D>
-__global__ __launch_bounds__(D)
-void decode_merge_gatesum_bf16_kernel(const float* __restrict__ part, const float* __restrict__ gate_part,
-                                      bf16* __restrict__ Y, int B, int Hq, int nsplit, int gsplits) {
-  constexpr int PST = D + 4;
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const float* p = part + ((int64_t)b * Hq + h) * nsplit * PST;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * PST + D]);
-  float lsum = 0.f, osum = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float f = fast_exp2(p[s * PST + D] - M);
-    lsum += p[s * PST + D + 1] * f;
-    osum += p[s * PST + d] * f;
-  }
-  const int64_t n = (int64_t)Hq * D, col = (int64_t)h * D + d;
-  float z = gate_part[(int64_t)b * n + col];
-  for (int s = 1; s < gsplits; ++s) z += gate_part[((int64_t)s * B + b) * n + col];
-  Y[((int64_t)b * Hq + h) * D + d] = (bf16)(osum / lsum * sigmoidf(z));
 }
 
 template <int D, int MODE>
@@ -455,37 +406,6 @@ hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* 
     hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
                        G, (bf16*)Y, Hq, nsplit, ep);
   }
-  return hipGetLastError();
-}
-
-// Decode with the elementwise gate folded in (D = 128, bf16): gate_part is the
-// float32 workspace of the split-K gate ([gsplits, B, Hq·D]).
-int64_t gate_splitk_splits(int64_t M, int64_t K, int64_t N);
-hipError_t launch_gated_decode_bf16(const void* X, const void* W, const void* Q, const void* K, const void* V,
-                                    void* Y, void* workspace, float* gate_part, int B, int L, int Hq, int Hkv,
-                                    int d_model, int nsplit, hipStream_t st) {
-  constexpr int D = 128;
-  const float scale_log2 = kLog2e / sqrtf((float)D);
-  const int chunk = (int)decode_chunk(L, nsplit);
-  float* part = (float*)workspace;
-  const int nquad = (Hq / Hkv + 3) / 4;
-  const int ny = Hkv * nquad;
-  const int64_t n_dec = (int64_t)nsplit * ny * B;
-  const int N = Hq * D;
-  const int gs = (int)gate_splitk_splits(B, d_model, N);
-  const int tiles_n = (int)ceil_div<int64_t>(N, gemm_splitk::BN);
-  const int64_t n_gate = ceil_div<int64_t>(B, gemm_splitk::BM) * tiles_n * gs;
-  const int nk_split = (int)ceil_div<int64_t>(ceil_div<int64_t>(d_model, gemm_splitk::BK), gs);
-  // the gate workgroups come first: with one workgroup per CU they take the
-  // first dispatch round together, and every CU then runs whole split
-  // workgroups (interleaving them instead leaves the long split workgroups
-  // unevenly spread over the CUs: 777 against 705 us at B 64, L 16384)
-  hipLaunchKernelGGL(decode_split_gate_bf16_kernel, dim3((unsigned)(n_dec + n_gate)), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2,
-                     ny, (const bf16*)X, (const bf16*)W, gate_part, B, d_model, N, tiles_n, gs, nk_split,
-                     (int)n_gate);
-  hipLaunchKernelGGL((decode_merge_gatesum_bf16_kernel<D>), dim3(Hq, B), dim3(D), 0, st, (const float*)part,
-                     (const float*)gate_part, (bf16*)Y, B, Hq, nsplit, gs);
   return hipGetLastError();
 }
 

@@ -87,6 +87,13 @@ __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory");
 }
+// The same with the non-temporal cache policy, for data read once (the decode
+// cache stream): a plain read of 4 GiB reaches 6.0-6.5 TB/s, the same read
+// with this policy 7.0-7.25 TB/s.
+__device__ __forceinline__ void dma16_lds_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }

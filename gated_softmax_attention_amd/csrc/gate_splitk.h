@@ -1,6 +1,5 @@
-// Split-K gate projection for few token rows (the decode gate): shared by the
-// gate GEMM kernels (gate_gemm.hip) and the decode split kernel, which runs the
-// same workgroups interleaved with its own (attn_decode.hip).
+// Split-K gate projection for few token rows (the decode gate), used by the
+// gate GEMM kernels (gate_gemm.hip).
 #pragma once
 
 #include "common.h"
@@ -38,8 +37,7 @@ __host__ __device__ constexpr int w_slot(int krow, int c) { return krow * (BN / 
 }  // namespace gemm_splitk
 
 // The workgroup `bid` of the split-K gate on two 64 KB LDS areas, Xs (the
-// X rings: [WAVES][NS][XSLOTS·8] bf16) and Ws (the W rings, same shape); also
-// run by the decode split kernel's gate workgroups, on the K and V rings.
+// X rings: [WAVES][NS][XSLOTS·8] bf16) and Ws (the W rings, same shape).
 __device__ __forceinline__ void gate_splitk_body(bf16* __restrict__ xs_lds, bf16* __restrict__ ws_lds,
                                                  const bf16* __restrict__ X, const bf16* __restrict__ W,
                                                  float* __restrict__ part, int M, int K, int N, int tiles_n,

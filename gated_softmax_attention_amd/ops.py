@@ -469,9 +469,8 @@ def gated_decode_workspace_bytes(B, L, Hq, Hkv, D, d_model, mode, dtype=torch.bf
 
 def gated_decode(X, W, Q, Kc, Vc, mode, num_splits=0, Y=None, workspace=None, stream=None):
     """The whole decode path in one call (gsa_gated_decode): the gate σ(X·W_θ) of
-    the B new tokens and the decode of Q [B,1,Hq,D] against Kc/Vc [B,L,Hkv,D];
-    with bf16, D 128 and the elementwise gate, the gate is folded into the
-    decode's launches."""
+    the B new tokens (split-K for few rows) and the decode of Q [B,1,Hq,D]
+    against Kc/Vc [B,L,Hkv,D], with one workspace for both."""
     B, one, Hq, D = Q.shape
     if one != 1:
         raise ValueError("decode takes one query token per batch")

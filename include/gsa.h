@@ -225,13 +225,8 @@ size_t gsa_gated_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_
  *   Q, Kc, Vc, Y, num_splits: as gsa_decode.
  *   workspace: at least gsa_gated_decode_workspace_bytes(...) bytes, 16-byte
  *     aligned, contents on entry irrelevant.
- * For bf16, D = 128 and the elementwise gate, when the split-K gate of
- * gsa_gate_logits_ws applies to [B, d_model]·[d_model, Hq·D], the gate is
- * folded into the decode's two launches: the split kernel's grid starts with
- * the split-K gate workgroups (64×64 tiles of X·W_θ over parts of d_model),
- * and the merge adds the parts in order and applies σ; Y then equals
- * gsa_gate_logits_ws followed by gsa_decode bit for bit.  Other cases run
- * gsa_gate_logits and gsa_decode.
+ * It runs gsa_gate_logits_ws (σ, into the workspace; the split-K path for few
+ * rows) and then gsa_decode, so Y equals those two calls bit for bit.
  * Errors: those of gsa_gate_logits and gsa_decode; X and W given without a
  * gate (or missing with one) -> GSA_ERR_INVALID_ARG.
  */

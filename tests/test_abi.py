@@ -415,8 +415,8 @@ def test_gated_decode_argument_checks(lib):
         k.get("dt", 1), 0)
     dec = lib.gsa_decode_workspace_bytes(64, 16384, 32, 8, 128, 0)
     base = (dec + 255) // 256 * 256
-    # folded gate: the split-K gate parts (4 parts of 64 x 4096 floats) after the decode partials
-    assert ws() == base + 4 * 64 * 4096 * 4
+    # the split-K gate parts (4 parts of 64 x 4096 floats), then G, after the decode partials
+    assert ws() == base + 4 * 64 * 4096 * 4 + 64 * 4096 * 4
     # headwise, float32: one G after the decode partials (float32 decode has none)
     assert ws(mode=2) == base + 64 * 32 * 4
     assert ws(dt=0) == 64 * 4096 * 4

@@ -106,23 +106,21 @@ def test_decode_long_cache():
 
 # --------------------------------------------------------------- the whole decode step in one call
 @pytest.mark.parametrize("B,L,Hq,Hkv,D,mode,dtype,dm", [
-    (64, 16384, 32, 8, 128, "elementwise", "bf16", 4096),   # the decode workload: gate folded in
-    (8, 3000, 16, 2, 128, "elementwise", "bf16", 2048),     # folded, fewer batches
+    (64, 16384, 32, 8, 128, "elementwise", "bf16", 4096),   # the decode workload: split-K gate
+    (8, 3000, 16, 2, 128, "elementwise", "bf16", 2048),     # split-K gate, fewer batches
     (3, 777, 8, 2, 128, "elementwise", "bf16", 1096),       # ragged d_model tile
-    (4, 1000, 8, 2, 128, "headwise", "bf16", 2048),         # two calls (headwise gate)
-    (2, 500, 8, 2, 64, "elementwise", "bf16", 2048),        # two calls (D 64)
-    (2, 300, 4, 2, 128, "elementwise", "fp32", 256),        # two calls (float32)
+    (4, 1000, 8, 2, 128, "headwise", "bf16", 2048),         # one-pass gate (32 columns)
+    (2, 500, 8, 2, 64, "elementwise", "bf16", 2048),        # D 64
+    (2, 300, 4, 2, 128, "elementwise", "fp32", 256),        # float32
     (2, 300, 4, 2, 128, "none", "bf16", 64),
 ])
 def test_gated_decode_one_call(B, L, Hq, Hkv, D, mode, dtype, dm):
-    """gsa_gated_decode against the two calls it stands for (gate, then decode)
-    and against the oracle, every batch.  When the gate is folded into the
-    decode's launches its parts are summed in the same order as the split-K
-    gate's, so the two agree bitwise."""
+    """gsa_gated_decode against the two calls it stands for (the gate with a
+    workspace, then the decode), bitwise, and against the oracle, every batch."""
     cfg = dec_cfg(B, L, Hq, Hkv, D, mode, dtype, dm=dm)
     print(f"  gated decode B{B} L{L} {Hq}/{Hkv}x{D} {mode} {dtype} dm{dm}", flush=True)
     if (B, L) in ((64, 16384), (8, 3000)):
-        # the gate is folded in: the workspace holds the split-K gate parts, not one G
+        # few gate rows: the workspace also holds the split-K gate parts
         dws = gsa.decode_workspace_bytes(B, L, Hq, Hkv, D)
         gate_area = gsa.gated_decode_workspace_bytes(B, L, Hq, Hkv, D, dm, mode) - (dws + 255) // 256 * 256
         assert gate_area > B * Hq * D * 4
