@@ -46,6 +46,11 @@ hipError_t launch_first_token_share(const void* Q, const void* K, const float* L
                                     int B, int S, int Hq, int Hkv, int D, bool bf16_inputs, hipStream_t st);
 size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int64_t gate_splitk_splits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gate_gemm_splitk_parts(const void* X, const void* W, float* part, int64_t M, int64_t K, int64_t N,
+                                         hipStream_t stream);
+hipError_t launch_decode_gateparts_bf16(const void* Q, const void* K, const void* V, const float* gate_part,
+                                        int gsplits, void* Y, void* workspace, int B, int L, int Hq, int Hkv, int D,
+                                        int nsplit, hipStream_t st);
 hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
                                    int64_t N, int act, hipStream_t stream);
 hipError_t launch_attn_fwd_value_gated(const void* Q, const void* K, const void* V, const float* Gv, void* Y,
@@ -443,6 +448,7 @@ gsa_status gsa_gated_decode(const void* X, const void* W, const void* Q, const v
   if (gsa_status st = check_attn_shape(fn, B, L, Hq, Hkv, D, mode, gated ? (const float*)W : nullptr, 1)) return st;
   if (gsa_status st = check_dtype(fn, dtype)) return st;
   if (num_splits < 0) return fail(GSA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  if (!prod_le({B, L}, kIntMax)) return fail(GSA_ERR_UNSUPPORTED, "%s: B*L exceeds the supported range", fn);
   if (gated && (d_model <= 0 || d_model > kIntMax))
     return fail(GSA_ERR_INVALID_ARG, "%s: d_model=%lld must be positive", fn, (long long)d_model);
   if (gated && d_model % 8 != 0)
@@ -459,8 +465,22 @@ gsa_status gsa_gated_decode(const void* X, const void* W, const void* Q, const v
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GSA_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
   if (gsa_status st = check_device()) return st;
-  // the gate into the workspace (split-K for few rows), then the decode
   char* ws = (char*)workspace;
+  // bf16, elementwise, split-K gate: its partial logits go to the workspace and
+  // the decode merge adds them and applies σ (one launch fewer than the part
+  // sum kernel; the same operations in the same order)
+  if (dtype == GSA_BF16 && mode == GSA_GATE_ELEMENTWISE && plan.gws_bytes > 0) {
+    const int64_t N = Hq * D;
+    const int64_t gs = gsa::gate_splitk_splits(B, d_model, N);
+    float* gparts = (float*)(ws + plan.gws_off);
+    hipError_t e = gsa::launch_gate_gemm_splitk_parts(X, W, gparts, B, d_model, N, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_result(e, fn);
+    const int64_t ns = gsa_decode_num_splits(B, L, Hq, Hkv, D, num_splits);
+    return hip_result(gsa::launch_decode_gateparts_bf16(Q, Kc, Vc, gparts, (int)gs, Y, ws, (int)B, (int)L, (int)Hq,
+                                                        (int)Hkv, (int)D, (int)ns, (hipStream_t)stream),
+                      fn);
+  }
+  // otherwise the gate into the workspace, then the decode
   float* G = gated ? (float*)(ws + plan.g_off) : nullptr;
   if (gated) {
     const int64_t N = mode == GSA_GATE_HEADWISE ? Hq : Hq * D;

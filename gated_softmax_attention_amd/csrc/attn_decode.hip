@@ -278,6 +278,33 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
                        blockIdx.z);
 }
 
+// The merge for the whole gated decode step (elementwise gate, bf16): the
+// gate's split-K partial logits are added here, in part order, and σ applied,
+// so O*/l*·σ(Σ_s gate_part[s]) is rounded once.  The same operations in the
+// same order as the part sum of the split-K gate followed by the plain merge.
+template <int D>
+__global__ __launch_bounds__(D)
+void decode_merge_gatesum_bf16_kernel(const float* __restrict__ part, const float* __restrict__ gate_part,
+                                      bf16* __restrict__ Y, int B, int Hq, int nsplit, int gsplits) {
+  constexpr int PST = D + 4;
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const float* p = part + ((int64_t)b * Hq + h) * nsplit * PST;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * PST + D]);
+  float lsum = 0.f, osum = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = fast_exp2(p[s * PST + D] - M);
+    lsum += p[s * PST + D + 1] * f;
+    osum += p[s * PST + d] * f;
+  }
+  const int64_t n = (int64_t)Hq * D, col = (int64_t)h * D + d;
+  float z = gate_part[(int64_t)b * n + col];
+  for (int s = 1; s < gsplits; ++s) z += gate_part[((int64_t)s * B + b) * n + col];
+  float y = osum / lsum;
+  y *= sigmoidf(z);
+  Y[((int64_t)b * Hq + h) * D + d] = (bf16)y;
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(D)
 void decode_merge_bf16_kernel(const float* __restrict__ part, const float* __restrict__ Gate,
@@ -405,6 +432,30 @@ hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* 
                        (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
     hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
                        G, (bf16*)Y, Hq, nsplit, ep);
+  }
+  return hipGetLastError();
+}
+
+// Decode with the elementwise gate given as gsplits float32 partial logits
+// ([gsplits, B, Hq·D], from the split-K gate): the split kernel, then the merge
+// that adds the parts and applies σ.
+hipError_t launch_decode_gateparts_bf16(const void* Q, const void* K, const void* V, const float* gate_part,
+                                        int gsplits, void* Y, void* workspace, int B, int L, int Hq, int Hkv, int D,
+                                        int nsplit, hipStream_t st) {
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  const int chunk = (int)decode_chunk(L, nsplit);
+  float* part = (float*)workspace;
+  const int nquad = (Hq / Hkv + 3) / 4;
+  if (D == 128) {
+    hipLaunchKernelGGL((decode_split_bf16_kernel<128>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    hipLaunchKernelGGL((decode_merge_gatesum_bf16_kernel<128>), dim3(Hq, B), dim3(128), 0, st, (const float*)part,
+                       gate_part, (bf16*)Y, B, Hq, nsplit, gsplits);
+  } else {
+    hipLaunchKernelGGL((decode_split_bf16_kernel<64>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    hipLaunchKernelGGL((decode_merge_gatesum_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
+                       gate_part, (bf16*)Y, B, Hq, nsplit, gsplits);
   }
   return hipGetLastError();
 }

@@ -581,8 +581,10 @@ size_t gate_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   return s > 0 ? (size_t)(s * M * N) * sizeof(float) : 0;
 }
 
-hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
-                                   int64_t N, int act, hipStream_t stream) {
+// The split-K partial logits alone ([s, M, N] float32 into part), for a
+// consumer that adds them itself (the decode merge).
+hipError_t launch_gate_gemm_splitk_parts(const void* X, const void* W, float* part, int64_t M, int64_t K, int64_t N,
+                                         hipStream_t stream) {
   using namespace gemm_splitk;
   const int64_t s = gate_splitk_splits(M, K, N);
   const int tiles_n = (int)ceil_div<int64_t>(N, BN);
@@ -591,6 +593,13 @@ hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float
   const int nk_split = (int)ceil_div<int64_t>(nk_all, s);
   hipLaunchKernelGGL(gate_gemm_bf16_splitk_kernel, dim3((unsigned)(tiles * s)), dim3(256), 0, stream,
                      (const bf16*)X, (const bf16*)W, part, (int)M, (int)K, (int)N, tiles_n, (int)s, nk_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_gemm_splitk(const void* X, const void* W, float* G, float* part, int64_t M, int64_t K,
+                                   int64_t N, int act, hipStream_t stream) {
+  const int64_t s = gate_splitk_splits(M, K, N);
+  if (hipError_t e = launch_gate_gemm_splitk_parts(X, W, part, M, K, N, stream); e != hipSuccess) return e;
   const int64_t n4 = M * N / 4;
   hipLaunchKernelGGL(gate_splitk_sum_kernel, dim3((unsigned)ceil_div<int64_t>(n4, 256)), dim3(256), 0, stream,
                      (const float*)part, G, n4, n4, (int)s, act);

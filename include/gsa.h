@@ -225,8 +225,10 @@ size_t gsa_gated_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_
  *   Q, Kc, Vc, Y, num_splits: as gsa_decode.
  *   workspace: at least gsa_gated_decode_workspace_bytes(...) bytes, 16-byte
  *     aligned, contents on entry irrelevant.
- * It runs gsa_gate_logits_ws (σ, into the workspace; the split-K path for few
- * rows) and then gsa_decode, so Y equals those two calls bit for bit.
+ * It computes what gsa_gate_logits_ws (σ, into the workspace; the split-K path
+ * for few rows) followed by gsa_decode computes, bit for bit; with bf16, the
+ * elementwise gate and the split-K path the decode merge adds the gate's
+ * partial logits itself (in part order) and applies σ, one launch fewer.
  * Errors: those of gsa_gate_logits and gsa_decode; X and W given without a
  * gate (or missing with one) -> GSA_ERR_INVALID_ARG.
  */
