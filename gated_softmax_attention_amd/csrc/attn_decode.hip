@@ -5,12 +5,16 @@
 // autoregressive decoding are from the §1.3.1 GQA explainer, and GQA lets a
 // group of query heads share each cached key/value head.
 //
-// Split kernel: workgroup (split s, key/value head c, batch b, quad of query
-// heads) streams keys [s*chunk, (s+1)*chunk) of head c once and serves up to 4
-// query heads of c's group.  The keys move global -> LDS in 64-key stages
-// (K and V, 32 KB for D = 128) through a ring of 4 stages filled by 16-byte
-// direct loads, so ~96 KB per workgroup stay in flight independent of the
-// register file.  Each wave takes 16 keys of a stage:
+// Split kernel: workgroup (split s, key/value heads, batch b, quad of query
+// heads) streams keys [s*chunk, (s+1)*chunk) once and serves up to 4 query
+// heads of each key/value head's group.  When 4 divides the key/value head
+// count a workgroup takes 4 adjacent heads, one per wave, and a stage holds 16
+// keys of all 4 (each key's 4-head row is one contiguous 1 KB read at D = 128;
+// 7.0 TB/s against 6.7 with one head's 256-byte rows); otherwise it takes one
+// head and each wave 16 keys of a 64-key stage.  Either way a stage is 32 KB
+// of K and V (D = 128) moving global -> LDS through a ring of 4 stages filled
+// by 16-byte direct loads, so ~96 KB per workgroup stay in flight independent
+// of the register file.  Per wave and 16 keys:
 //   S = Q·Kᵀ on v_mfma_f32_16x16x32_bf16 with the (≤4) query rows replicated
 //     over the 16 MFMA rows, so every lane ends up holding the 4 heads' scores
 //     for "its" key;
@@ -20,8 +24,9 @@
 //     of the 128 dims (reduced over the 16 key lanes once, at the end).
 // LDS rows are 16-byte-chunk swizzled (chunk ^= key & 15) so the 16 keys a
 // wave reads at one chunk hit distinct banks.
-// The workgroup merges its 4 waves' (m, l, O) through LDS and writes one
-// float32 partial (O, m, l) per query head.  The merge kernel combines the
+// With one head per workgroup the 4 waves' (m, l, O) are merged through LDS;
+// with 4, each wave's own (m, l, O) is final.  Either way one float32 partial
+// (O, m, l) is written per query head and split.  The merge kernel combines the
 // splits exactly: m* = max m_s, l* = Σ l_s 2^{m_s − m*}, O* = Σ O_s 2^{m_s − m*},
 // then O*/l* times the gate, rounded once to bf16.
 #include "common.h"
@@ -68,8 +73,12 @@ struct DecSmem {
   float sm_o[dec::WAVES][4][D];
 };
 
-// The split workgroup (split s, key/value head and quad yq, batch b) on the LDS sm.
-template <int D>
+// The split workgroup (split s, key/value head group and quad yq, batch b) on
+// the LDS sm.  HW = 1: the workgroup takes one key/value head and its 4 waves
+// take 16 keys each of a 64-key stage; HW = 4: it takes 4 adjacent key/value
+// heads, wave w the (w+1)-th, and a stage holds 16 keys of all 4, so each key's
+// cached row of the 4 heads (4·D·2 bytes) is read as one contiguous piece.
+template <int D, int HW>
 __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
                                                   float* __restrict__ part, int L, int Hq, int Hkv, int nsplit,
@@ -85,18 +94,21 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kl = lane & 15, jg = lane >> 4;
+  static_assert(HW == 1 || HW == WAVES, "one key/value head per workgroup, or one per wave");
   const int G = Hq / Hkv;
   const int nquad = (G + 3) / 4;
-  const int c = yq / nquad, quad = yq % nquad;
+  const int c0 = (yq / nquad) * HW, quad = yq % nquad;   // the workgroup's first key/value head
+  const int c = HW == 1 ? c0 : c0 + wave;                 // this wave's key/value head
   const int h0 = c * G + quad * 4;
   const int nq = min(4, G - quad * 4);
+  constexpr int TKS = HW == 1 ? TK : KB;                  // keys per stage
 
   const int key_begin = s * chunk;
   const int key_end = min(L, key_begin + chunk);
 
   const int64_t kv_row = (int64_t)Hkv * D;
-  const bf16* Kb = Kc + (int64_t)b * L * kv_row + (int64_t)c * D;
-  const bf16* Vb = Vc + (int64_t)b * L * kv_row + (int64_t)c * D;
+  const bf16* Kb = Kc + (int64_t)b * L * kv_row + (int64_t)c0 * D;
+  const bf16* Vb = Vc + (int64_t)b * L * kv_row + (int64_t)c0 * D;
 
   // A operand: MFMA row m = kl holds query slot kl % 4 (rows replicated 4x)
   bf16x8 qa[NKK];
@@ -123,27 +135,30 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
       for (int e = 0; e < 8; ++e) o[r][kk][e] = 0.f;
   }
 
-  // ---- LDS ring of NS stages, each K[TK][D] and V[TK][D], chunk-swizzled rows
-  constexpr int CHK = D / 8;                         // 16-byte chunks per row
+  // ---- LDS ring of NS stages, each K[TKS][HW·D] and V[TKS][HW·D]; a stage row
+  // is one key of the HW heads, each head's D values chunk-swizzled by key
+  constexpr int CHK = D / 8;                         // 16-byte chunks per head and key
+  constexpr int RCH = HW * CHK;                      // chunks per stage row
   auto& Ks = sm.Ks;
   auto& Vs = sm.Vs;
+  static_assert(TKS * RCH == TK * CHK, "a stage holds the same bytes in either arrangement");
   constexpr int NI = TK * CHK / 64 / WAVES;          // direct loads per wave, stage and tensor
   const uint32_t row_b = (uint32_t)(kv_row * 2);
-  const uint32_t kv_bytes = (uint32_t)(((int64_t)L * kv_row - (int64_t)c * D) * 2);
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)L * kv_row - (int64_t)c0 * D) * 2);
   const auto krs = make_rsrc(Kb, kv_bytes);          // keys >= L read as zeros
   const auto vrs = make_rsrc(Vb, kv_bytes);
   uint32_t dma_off[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int sl = (wave + WAVES * i) * 64 + lane;
-    const int row = sl / CHK, phys = sl % CHK;
-    dma_off[i] = (uint32_t)row * row_b + (uint32_t)((phys ^ (row & (CHK - 1))) * 16);
+    const int row = sl / RCH, hw = (sl % RCH) / CHK, phys = sl % CHK;
+    dma_off[i] = (uint32_t)row * row_b + (uint32_t)(hw * D * 2) + (uint32_t)((phys ^ (row & (CHK - 1))) * 16);
   }
   const int nkeys = key_end - key_begin;
-  const int n_st = ceil_div(nkeys, TK);
+  const int n_st = ceil_div(nkeys, TKS);
   auto dma = [&](int st) {
     const int buf = st % NS;
-    const uint32_t base = (uint32_t)(key_begin + st * TK) * row_b;
+    const uint32_t base = (uint32_t)(key_begin + st * TKS) * row_b;
     const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[buf][0]));
     const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[buf][0]));
 #pragma unroll
@@ -159,8 +174,9 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
     else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NI) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  // this lane's key row within a stage and its operand chunks
-  const int my_row = wave * KB + kl;
+  // this lane's key row within a stage, and where this wave's head starts in it
+  const int my_row = HW == 1 ? wave * KB + kl : kl;
+  const int head_chunk = HW == 1 ? 0 : wave * CHK;
 
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
@@ -170,13 +186,13 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
     __syncthreads();                                 // stage t complete; stage t-1 free
     if (t + NS - 1 < n_st) dma(t + NS - 1);
     const int buf = t % NS;
-    const int key = key_begin + t * TK + my_row;
+    const int key = key_begin + t * TKS + my_row;
     u32x4 kcur[NKK], vcur[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int ch = (4 * kk + jg) ^ (my_row & (CHK - 1));
-      kcur[kk] = *(const u32x4*)(&Ks[buf][my_row * D + ch * 8]);
-      vcur[kk] = *(const u32x4*)(&Vs[buf][my_row * D + ch * 8]);
+      const int ch = head_chunk + ((4 * kk + jg) ^ (my_row & (CHK - 1)));
+      kcur[kk] = *(const u32x4*)(&Ks[buf][(my_row * RCH + ch) * 8]);
+      vcur[kk] = *(const u32x4*)(&Vs[buf][(my_row * RCH + ch) * 8]);
     }
 
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -230,6 +246,26 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[r][kk][e] = row16_sum(o[r][kk][e]);
   }
+  if constexpr (HW != 1) {
+    // each wave has its own query heads and saw every key of the split: its
+    // (O, m, l) is the record
+    if (kl == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r >= nq) continue;
+        float* rec = part + (((int64_t)b * Hq + h0 + r) * nsplit + s) * PST;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rec[32 * kk + 8 * jg + e] = o[r][kk][e];
+        if (jg == 0) {
+          rec[D] = m_run[r];
+          rec[D + 1] = l_run[r];
+        }
+      }
+    }
+    return;
+  }
   if (kl == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -268,14 +304,33 @@ __device__ __forceinline__ void decode_split_body(DecSmem<D>& sm, const bf16* __
   }
 }
 
-template <int D>
+template <int D, int HW>
 __global__ __launch_bounds__(256)
 void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc,
                               const bf16* __restrict__ Vc, float* __restrict__ part,
                               int L, int Hq, int Hkv, int nsplit, int chunk, float scale_log2) {
   __shared__ __align__(16) DecSmem<D> sm;
-  decode_split_body<D>(sm, Q, Kc, Vc, part, L, Hq, Hkv, nsplit, chunk, scale_log2, blockIdx.x, blockIdx.y,
-                       blockIdx.z);
+  decode_split_body<D, HW>(sm, Q, Kc, Vc, part, L, Hq, Hkv, nsplit, chunk, scale_log2, blockIdx.x, blockIdx.y,
+                           blockIdx.z);
+}
+
+#ifndef GSA_DEC_HW
+#define GSA_DEC_HW 4
+#endif
+// Key/value heads per split workgroup: 4 when they divide Hkv (each key's row
+// of the 4 heads is one contiguous read), else 1.
+int decode_heads_per_workgroup(int64_t Hkv) { return (GSA_DEC_HW == 4 && Hkv % 4 == 0) ? 4 : 1; }
+
+template <int D>
+static void launch_split(const void* Q, const void* K, const void* V, float* part, int B, int L, int Hq, int Hkv,
+                         int nsplit, int chunk, float scale_log2, hipStream_t st) {
+  const int nquad = (Hq / Hkv + 3) / 4;
+  if (decode_heads_per_workgroup(Hkv) == 4)
+    hipLaunchKernelGGL((decode_split_bf16_kernel<D, 4>), dim3(nsplit, (Hkv / 4) * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+  else
+    hipLaunchKernelGGL((decode_split_bf16_kernel<D, 1>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
 }
 
 // The merge for the whole gated decode step (elementwise gate, bf16): the
@@ -377,11 +432,14 @@ void decode_merge_variant_bf16_kernel(const float* __restrict__ part, const floa
 
 int64_t decode_auto_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv) {
   const int64_t G = Hq / Hkv;
-  const int64_t base = B * Hkv * ((G + 3) / 4);
-  // aim for >= 1024 workgroups: one fits a CU (its LDS ring), so that is about
-  // four dispatch rounds on 256 CUs; more splits add rounds and partials
-  // without adding bytes in flight
-  int64_t ns = (1024 + base - 1) / base;
+  const int hw = decode_heads_per_workgroup(Hkv);
+  const int64_t base = B * (Hkv / hw) * ((G + 3) / 4);
+  // One workgroup fits a CU (its LDS ring).  With 4 heads per workgroup aim
+  // for one round on the 256 CUs (B 64, L 16384, 8 KV heads: 2 splits, 613 us,
+  // against 636 us for 512 workgroups and 661 us for 1024); with one head per
+  // workgroup for about 1024 (there 1024 workgroups ran 643 us, 512 ran 661 us).
+  const int64_t target = hw == 4 ? 256 : 1024;
+  int64_t ns = (target + base - 1) / base;
   const int64_t max_ns = (L + 255) / 256;          // but at least 256 keys per split
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
@@ -398,11 +456,7 @@ template <int D>
 static void launch_dec(const void* Q, const void* K, const void* V, const float* G, void* Y,
                        float* part, int B, int L, int Hq, int Hkv, int mode, int nsplit,
                        int chunk, float scale_log2, hipStream_t st) {
-  const int Gq = Hq / Hkv;
-  const int nquad = (Gq + 3) / 4;
-  hipLaunchKernelGGL((decode_split_bf16_kernel<D>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit,
-                     chunk, scale_log2);
+  launch_split<D>(Q, K, V, part, B, L, Hq, Hkv, nsplit, chunk, scale_log2, st);
   if (mode == kDecGateElem)
     hipLaunchKernelGGL((decode_merge_bf16_kernel<D, kDecGateElem>), dim3(Hq, B), dim3(D), 0, st,
                        (const float*)part, G, (bf16*)Y, Hq, nsplit);
@@ -420,16 +474,13 @@ hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* 
   const float scale_log2 = kLog2e / sqrtf((float)D);
   const int chunk = (int)decode_chunk(L, nsplit);
   float* part = (float*)workspace;
-  const int nquad = (Hq / Hkv + 3) / 4;
   const DecEpi ep{layout, add, rms};
   if (D == 128) {
-    hipLaunchKernelGGL((decode_split_bf16_kernel<128>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
-                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    launch_split<128>(Q, K, V, part, B, L, Hq, Hkv, nsplit, chunk, scale_log2, st);
     hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<128>), dim3(Hq, B), dim3(128), 0, st, (const float*)part,
                        G, (bf16*)Y, Hq, nsplit, ep);
   } else {
-    hipLaunchKernelGGL((decode_split_bf16_kernel<64>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
-                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    launch_split<64>(Q, K, V, part, B, L, Hq, Hkv, nsplit, chunk, scale_log2, st);
     hipLaunchKernelGGL((decode_merge_variant_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
                        G, (bf16*)Y, Hq, nsplit, ep);
   }
@@ -445,15 +496,12 @@ hipError_t launch_decode_gateparts_bf16(const void* Q, const void* K, const void
   const float scale_log2 = kLog2e / sqrtf((float)D);
   const int chunk = (int)decode_chunk(L, nsplit);
   float* part = (float*)workspace;
-  const int nquad = (Hq / Hkv + 3) / 4;
   if (D == 128) {
-    hipLaunchKernelGGL((decode_split_bf16_kernel<128>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
-                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    launch_split<128>(Q, K, V, part, B, L, Hq, Hkv, nsplit, chunk, scale_log2, st);
     hipLaunchKernelGGL((decode_merge_gatesum_bf16_kernel<128>), dim3(Hq, B), dim3(128), 0, st, (const float*)part,
                        gate_part, (bf16*)Y, B, Hq, nsplit, gsplits);
   } else {
-    hipLaunchKernelGGL((decode_split_bf16_kernel<64>), dim3(nsplit, Hkv * nquad, B), dim3(256), 0, st,
-                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, part, L, Hq, Hkv, nsplit, chunk, scale_log2);
+    launch_split<64>(Q, K, V, part, B, L, Hq, Hkv, nsplit, chunk, scale_log2, st);
     hipLaunchKernelGGL((decode_merge_gatesum_bf16_kernel<64>), dim3(Hq, B), dim3(64), 0, st, (const float*)part,
                        gate_part, (bf16*)Y, B, Hq, nsplit, gsplits);
   }

@@ -154,39 +154,83 @@ def test_forward_tiles(D):
 
 
 # ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("HW", [1, 4])
 @pytest.mark.parametrize("D", [64, 128])
-def test_decode_ring(D):
+def test_decode_ring(D, HW):
+    """The split kernel's stage: TKS key rows of HW heads' D values, each head's
+    16-byte chunks swizzled by key; HW = 1 (one head, 4 waves x 16 keys of a
+    64-key stage) or HW = 4 (4 heads, one per wave, 16 keys a stage)."""
     pinned("attn_decode.hip",
            "constexpr int KB = 16;", "constexpr int WAVES = 4;", "constexpr int TK = KB * WAVES;",
            "constexpr int NS = 4;",
-           "constexpr int CHK = D / 8;",
+           "constexpr int TKS = HW == 1 ? TK : KB;",
+           "constexpr int CHK = D / 8;", "constexpr int RCH = HW * CHK;",
            "bf16 Ks[dec::NS][dec::TK * D];", "auto& Ks = sm.Ks;",
            "constexpr int NI = TK * CHK / 64 / WAVES;",
-           "const int sl = (wave + WAVES * i) * 64 + lane; const int row = sl / CHK, phys = sl % CHK; "
-           "dma_off[i] = (uint32_t)row * row_b + (uint32_t)((phys ^ (row & (CHK - 1))) * 16);",
+           "const int sl = (wave + WAVES * i) * 64 + lane; const int row = sl / RCH, hw = (sl % RCH) / CHK, "
+           "phys = sl % CHK; dma_off[i] = (uint32_t)row * row_b + (uint32_t)(hw * D * 2) + "
+           "(uint32_t)((phys ^ (row & (CHK - 1))) * 16);",
            "const uint32_t ins = (uint32_t)(wave + WAVES * i) * 64 * 16;",
-           "const int my_row = wave * KB + kl;",
-           "const int ch = (4 * kk + jg) ^ (my_row & (CHK - 1)); kcur[kk] = *(const u32x4*)(&Ks[buf][my_row * D + ch * 8]);")
+           "const int my_row = HW == 1 ? wave * KB + kl : kl;",
+           "const int head_chunk = HW == 1 ? 0 : wave * CHK;",
+           "const int ch = head_chunk + ((4 * kk + jg) ^ (my_row & (CHK - 1))); "
+           "kcur[kk] = *(const u32x4*)(&Ks[buf][(my_row * RCH + ch) * 8]);",
+           "const int c = HW == 1 ? c0 : c0 + wave;",
+           "const uint32_t kv_bytes = (uint32_t)(((int64_t)L * kv_row - (int64_t)c0 * D) * 2);")
     KB, WAVES, CHK = 16, 4, D // 8
     TK = KB * WAVES
+    TKS = TK if HW == 1 else KB
+    RCH = HW * CHK
     NI = TK * CHK // 64 // WAVES
     assert NI * 64 * WAVES == TK * CHK                       # whole instructions
-    kmap = check_loader(NI * WAVES, TK * CHK, lambda s: (s // CHK, (s % CHK) ^ ((s // CHK) & (CHK - 1))), TK, CHK)
+    assert TKS * RCH == TK * CHK                             # the stage holds TK·D bf16 in either arrangement
+    # slot -> (row, head·CHK + logical chunk) written there
+    lmap = check_loader(NI * WAVES, TK * CHK,
+                        lambda s: (s // RCH, ((s % RCH) // CHK) * CHK + ((s % CHK) ^ ((s // RCH) & (CHK - 1)))),
+                        TKS, RCH)
+    # global byte offset of a slot (relative to the workgroup's first head of key 0): it must be the
+    # bytes of the (row, head, chunk) that the slot holds, row_b = Hkv·D·2 with Hkv = 8
+    row_b = 8 * D * 2
+    for s_ in range(NI * WAVES * 64):
+        row, hw, phys = s_ // RCH, (s_ % RCH) // CHK, s_ % CHK
+        off = row * row_b + hw * D * 2 + (phys ^ (row & (CHK - 1))) * 16
+        r, q = next(k for k, v in lmap.items() if v == s_)
+        assert off == r * row_b + (q // CHK) * D * 2 + (q % CHK) * 16
     worst = 0
     for wave in range(WAVES):
         for kk in range(D // 32):
             addrs = []
             for lane in range(64):
                 kl, jg = lane & 15, lane >> 4
-                my_row = wave * KB + kl
-                ch = (4 * kk + jg) ^ (my_row & (CHK - 1))
-                a = (my_row * D + ch * 8) * 2
-                assert a + 16 <= TK * D * 2 and kmap[(my_row, 4 * kk + jg)] * 16 == a
+                my_row = wave * KB + kl if HW == 1 else kl
+                head_chunk = 0 if HW == 1 else wave * CHK
+                ch = head_chunk + ((4 * kk + jg) ^ (my_row & (CHK - 1)))
+                a = (my_row * RCH + ch) * 16
+                assert a + 16 <= TK * D * 2
+                # the slot read holds this lane's key row, its wave's head and chunk 4kk + jg
+                assert lmap[(my_row, head_chunk + 4 * kk + jg)] * 16 == a
                 addrs.append(a)
             for g in range(0, 64, 16):
                 worst = max(worst, conflicts(addrs[g:g + 16], 16))
-    # 128-byte rows at D = 64: 16 lanes span 2 KB, so rows l and l + 8 share banks
+    # rows a multiple of 256 B apart: 16 lanes spread over 16 chunks (D = 128) or 8 (D = 64)
     assert worst == (1 if D == 128 else 2)
+
+
+def test_decode_ring_reads_stay_in_the_cache():
+    """Every direct load of the 4-head arrangement reads bytes of heads c0 .. c0+3
+    of a key < L, or lies past the range check (keys >= L): with c0 + 3 < Hkv the
+    furthest byte of a valid key is inside kv_bytes."""
+    for D in (64, 128):
+        for Hkv in (4, 8, 16):
+            for c0 in range(0, Hkv, 4):
+                L = 37
+                row_b = Hkv * D * 2
+                kv_bytes = L * row_b - c0 * D * 2
+                for key in range(L):
+                    for hw in range(4):
+                        last = key * row_b + hw * D * 2 + D * 2 - 1
+                        assert last < kv_bytes
+                assert L * row_b >= kv_bytes      # the first byte of key L is past the range
 
 
 # ------------------------------------------------------------------ gate GEMM, 256x256 tiles
