@@ -34,8 +34,11 @@ def oracle_decode(inp, mode, batches=None):
 
 
 CASES = []
+# (Hkv a multiple of 4 takes the 4-heads-per-workgroup split kernel; with
+# groups of 6, 8 and 12 query heads it also serves 2 or 3 quads, the last partial)
 for (B, L, Hq, Hkv) in [(1, 1, 4, 1), (2, 15, 4, 4), (3, 16, 8, 2), (2, 63, 8, 1), (1, 1025, 32, 8),
-                        (2, 3000, 16, 2), (4, 777, 12, 2), (1, 4096, 4, 4)]:
+                        (2, 3000, 16, 2), (4, 777, 12, 2), (1, 4096, 4, 4), (2, 1500, 32, 4), (1, 700, 48, 4),
+                        (3, 333, 24, 4), (1, 2000, 16, 16)]:
     for D in (128, 64):
         for mode in ("elementwise", "headwise"):
             CASES.append((B, L, Hq, Hkv, D, mode))
