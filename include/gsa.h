@@ -152,7 +152,9 @@ gsa_status gsa_forward_lse(const void* Q, const void* K, const void* V, const fl
 
 /*
  * Split count gsa_decode will use for these sizes: num_splits itself if > 0,
- * otherwise the automatic choice.  Returns 0 for invalid sizes.
+ * otherwise the automatic choice (about one split workgroup per CU when 4
+ * divides Hkv, about four otherwise; at least 256 keys per split), rounded so
+ * that every split gets keys.  Returns 0 for invalid sizes.
  */
 int64_t gsa_decode_num_splits(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
                               int num_splits);
