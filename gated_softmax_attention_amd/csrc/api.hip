@@ -243,6 +243,8 @@ gsa_status gsa_gate_logits_ws(const void* X, const void* W, float* G, int64_t M,
                     fn);
 }
 
+}  // extern "C"
+
 namespace {
 gsa_status forward_impl(const char* fn, const void* Q, const void* K, const void* V, const float* G,
                         void* Y, float* LSE, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
@@ -260,6 +262,8 @@ gsa_status forward_impl(const char* fn, const void* Q, const void* K, const void
                     fn);
 }
 }  // namespace
+
+extern "C" {
 
 gsa_status gsa_forward(const void* Q, const void* K, const void* V, const float* G, void* Y,
                        int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int mode, int dtype,
@@ -399,6 +403,8 @@ gsa_status gsa_decode_noalloc(const void* Q, const void* Kc, const void* Vc, con
                     fn);
 }
 
+}  // extern "C"
+
 namespace {
 // gsa_gated_decode's workspace: [decode partials | split-K gate parts | G],
 // each 256-byte aligned (the gate parts only when gsa_gate_logits_ws takes its
@@ -423,6 +429,8 @@ GatedDecodePlan gated_decode_plan(int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
   return p;
 }
 }  // namespace
+
+extern "C" {
 
 size_t gsa_gated_decode_workspace_bytes(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t d_model,
                                         int mode, int dtype, int num_splits) {
@@ -530,6 +538,8 @@ gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, con
                     fn);
 }
 
+}  // extern "C"
+
 namespace {
 // Workspace of gsa_backward, each region 256-byte aligned:
 //   dY  = dY' ⊙ g                 bf16 [B, S, Hq, D]          (gated modes)
@@ -570,6 +580,8 @@ BwdLayout bwd_layout(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, i
 }
 constexpr int64_t kU32Bytes = 0xfffffff0LL;   // operands addressed with 32-bit byte offsets
 }  // namespace
+
+extern "C" {
 
 size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                     int64_t d_model, int mode) {

@@ -36,7 +36,6 @@
 
 namespace gsa {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.69314718055994531f;
 
 namespace fwd {
