@@ -343,20 +343,27 @@ void gate_gemm_bf16_big_kernel(const bf16* __restrict__ X, const bf16* __restric
   // epilogue: lane holds column l32 of each 32x32 block, rows 8*(r/4) + 4*hl + r%4
   const bool full = (m0 + BM <= M) && (n0 + BN <= N);
   if constexpr (!ROUTE) {
+    // one copy of the store loops per activation: no activation switch per element
+    auto store_all = [&](auto act_c) {
+      constexpr int A = decltype(act_c)::value;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int n = n0 + wn * 64 + nt * 32 + l32;
-        const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = n0 + wn * 64 + nt * 32 + l32;
+          const int mb = m0 + wm * 128 + mt * 32 + 4 * hl;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mb + 8 * (r >> 2) + (r & 3);
-          const float z = acc[mt][nt][r];
-          const float v = gate_act(z, act);
-          if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int m = mb + 8 * (r >> 2) + (r & 3);
+            const float v = gate_act(acc[mt][nt][r], A);
+            if (full || (m < M && n < N)) G[(int64_t)m * N + n] = v;
+          }
         }
-      }
+    };
+    if (act == kActSigmoid) store_all(std::integral_constant<int, kActSigmoid>{});
+    else if (act == kActNsSigmoid) store_all(std::integral_constant<int, kActNsSigmoid>{});
+    else if (act == kActSilu) store_all(std::integral_constant<int, kActSilu>{});
+    else store_all(std::integral_constant<int, kActIdentity>{});
   } else {
     const int ng = N - po.nq - 2 * po.nkv;
 #pragma unroll
