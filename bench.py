@@ -250,7 +250,9 @@ def decode_bench(args, torch, gsa, cfg, keep_batches=0):
         "config": {"workload": "decode", "B": cfg.B, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
                    "d_model": cfg.d_model, "mode": cfg.mode, "num_splits": ns, "bytes_per_step": nbytes["total"]},
         "roofline": {
-            "kernel": f"decode_split_bf16_kernel<{cfg.D}> + decode_merge_bf16_kernel (one gsa_decode call)",
+            # the library takes 4 key/value heads per split workgroup when 4 divides Hkv
+            "kernel": (f"decode_split_bf16_kernel<{cfg.D}, {4 if cfg.Hkv % 4 == 0 else 1}> + "
+                       f"decode_merge_bf16_kernel<{cfg.D}> (one gsa_decode call)"),
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": measured_traffic("decode_split", ["attn_decode.hip", "common.h"]),
