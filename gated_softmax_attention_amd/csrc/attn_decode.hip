@@ -314,9 +314,12 @@ void decode_split_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict
                            blockIdx.z);
 }
 
+// Building with -DGSA_DEC_HW=1 keeps one key/value head per split workgroup for
+// every head count (the arrangement the 4-head one is compared against).
 #ifndef GSA_DEC_HW
 #define GSA_DEC_HW 4
 #endif
+static_assert(GSA_DEC_HW == 4 || GSA_DEC_HW == 1, "GSA_DEC_HW is 4 or 1");
 // Key/value heads per split workgroup: 4 when they divide Hkv (each key's row
 // of the 4 heads is one contiguous read), else 1.
 int decode_heads_per_workgroup(int64_t Hkv) { return (GSA_DEC_HW == 4 && Hkv % 4 == 0) ? 4 : 1; }

@@ -53,13 +53,14 @@ def test_small_decode(B, L, Hq, Hkv, D, mode, dtype):
     report(f64(Y), oracle_decode(inp, mode), TOL[dtype], f"{dtype} B{B} L{L} {Hq}/{Hkv} D{D} {mode}")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8)])   # one key/value head per split workgroup, and four
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 16, 64])
-def test_split_counts_agree(ns):
-    inp = make_inputs(dec_cfg(2, 2049, 8, 2, 128, "elementwise", "bf16"), seed=9, device=DEV)
+def test_split_counts_agree(ns, Hq, Hkv):
+    inp = make_inputs(dec_cfg(2, 2049, Hq, Hkv, 128, "elementwise", "bf16"), seed=9, device=DEV)
     want = oracle_decode(inp, "elementwise")
     Y, _ = run(inp, "elementwise", num_splits=ns)
-    report(f64(Y), want, TOL["bf16"], f"splits {ns} (effective "
-           f"{gsa.decode_num_splits(2, 2049, 8, 2, 128, ns)})")
+    report(f64(Y), want, TOL["bf16"], f"{Hq}/{Hkv} heads, splits {ns} (effective "
+           f"{gsa.decode_num_splits(2, 2049, Hq, Hkv, 128, ns)})")
 
 
 def test_decode_matches_last_prefill_row():
