@@ -304,7 +304,10 @@ def backward_bench(args, torch, gsa, cfg):
         "roofline": {
             "kernel": "gsa_backward (prep + dQ + dK/dV + dX + dW kernels)", "bound": "mfma",
             "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "avg_launch_ms": ms,
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            # HBM bytes of one call, all its kernels summed
+            "traffic": measured_traffic("backward", ["attn_bwd.hip", "gemm_bwd.hip", "common.h"]),
+            "avg_launch_ms": ms,
             "algorithmic_flops_per_launch": flops,
         },
     }
@@ -444,7 +447,8 @@ def diagnostic_bench(args, torch, gsa, cfg):
                    "token0_key_scale": cfg.sink_scale},
         "roofline": {
             "kernel": "first_token_share_kernel (+ head means)", "bound": "hbm", "achieved": achieved,
-            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+            "traffic": measured_traffic("first_token", ["attn_diag.hip", "common.h"]),
             "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes,
         },
     }
