@@ -438,9 +438,38 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // both last read in iteration t-1, and are waited for before the barrier.
   // The body is one basic block apart from the mask (diagonal tiles only, at
   // the top) and the rare rescale, so the compiler interleaves the Sᵀ(t+1)
-  // matrix ops with the VALU work of softmax(t).  On the last tile Sᵀ(t+1)
-  // runs on whatever the K buffer holds and is discarded.
-  // iteration `it` with compile-time buffer parity P = it & 1
+  // matrix ops with the VALU work of softmax(t).  The last tile has a step of
+  // its own (last_step), so the loop body never computes an Sᵀ it discards.
+  //
+  // softmax(t) and PV(t) of the last tile, which has no next tile: no loads
+  // and no Sᵀ(t+1).  A wave whose rows all come before the tile's first key
+  // (one head per workgroup: the first waves' last tile) skips it: every score
+  // would be masked, so its p are 0 and O, l and the reference stay as they are.
+  auto last_step = [&](auto parity, int it, f32x16 (&cur)[2][QB]) {
+    constexpr int P = decltype(parity)::value;
+    bf16* const v_cur = P ? Vs1 : Vs0;   // V(t)
+    const int k0 = it * BN;
+    if (k0 <= qw0 + 32 * QB - 1) {
+      if ((k0 + BN - 1 > qw0) || (k0 + BN > S)) apply_mask(cur, k0);
+      const bool move = softmax_max(cur);
+      if (move) rescale_o();
+      bf16x8 pb[QB][2][2];
+      float ps[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ps[qb][0] = ps[qb][1] = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          exp_q(cur, pb, ps, sub, t);
+          pv_q(v_cur, pb, sub, t);
+        }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] = l_run[qb] * alpha[qb] + (ps[qb][0] + ps[qb][1]);
+    }
+    __syncthreads();   // every wave is past its last LDS read: the epilogue reuses the stage arrays
+  };
+  // iteration `it` (not the last) with compile-time buffer parity P = it & 1
   auto step = [&](auto parity, int it, f32x16 (&cur)[2][QB], f32x16 (&nxt)[2][QB]) {
     constexpr int P = decltype(parity)::value;
     bf16* const k_cur = P ? Ks1 : Ks0;   // held K(t), consumed in iteration t-1: refill with K(t+2)
@@ -497,10 +526,14 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   gate_v(Vs0);   // G2 only; published by the barrier below, before the first PV product
   mma_s(Ks0, sA);
   __syncthreads();   // K buffer 0 is refilled in the first iteration
-  for (int it = 0; it < n_kv; it += 2) {
+  // every tile but the last, then the last (its Sᵀ is in sA when its index is even)
+  const int n_main = n_kv - 1;
+  for (int it = 0; it < n_main; it += 2) {
     step(std::integral_constant<int, 0>{}, it, sA, sB);
-    if (it + 1 < n_kv) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
+    if (it + 1 < n_main) step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
   }
+  if (n_main & 1) last_step(std::integral_constant<int, 1>{}, n_main, sB);
+  else last_step(std::integral_constant<int, 0>{}, n_main, sA);
 
   if constexpr (QB == 1) {
     // Epilogue through LDS.  In the accumulator layout a lane holds one row and
