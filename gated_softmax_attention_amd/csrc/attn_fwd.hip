@@ -522,10 +522,20 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   dma_v(0, true, Vs0);
   dma_g(0, true);
   dma_k(BN, n_kv > 1, Ks1);
-  wait_dma_and_sync();
-  gate_v(Vs0);   // G2 only; published by the barrier below, before the first PV product
+  // Sᵀ(0) needs only Q and K(0): wait until at most this wave's later loads
+  // (V(0), its gate tile, K(1)) are outstanding, then for every wave's K(0),
+  // so the first score tile overlaps the rest of the prologue's loads
+  {
+    constexpr int kAfterK0 = VSL / 4 + (MODE == kValueGateElem ? GIW : 0) + (KSL + 3) / 4 - 1;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterK0) : "memory");
+    __builtin_amdgcn_s_barrier();
+  }
   mma_s(Ks0, sA);
-  __syncthreads();   // K buffer 0 is refilled in the first iteration
+  wait_dma_and_sync();   // V(0), its gate and K(1); K buffer 0 is refilled in the first iteration
+  if constexpr (kG2) {
+    gate_v(Vs0);
+    __syncthreads();     // V' of tile 0 before the first PV product
+  }
   // every tile but the last, then the last (its Sᵀ is in sA when its index is even)
   const int n_main = n_kv - 1;
   for (int it = 0; it < n_main; it += 2) {
