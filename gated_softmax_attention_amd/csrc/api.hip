@@ -27,7 +27,7 @@ int64_t decode_chunk(int64_t L, int64_t nsplit);
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
                            const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
-                           int mode, hipStream_t stream);
+                           int mode, hipStream_t stream, hipStream_t dq_stream, hipEvent_t fork);
 int bwd_kv_slices(int B, int S, int Hq, int Hkv, int D);
 hipError_t launch_decode_variant_bf16(const void* Q, const void* K, const void* V, const float* G, void* Y,
                                       void* workspace, int B, int L, int Hq, int Hkv, int D, int layout, int add,
@@ -541,6 +541,34 @@ gsa_status gsa_decode_variant(const void* Q, const void* Kc, const void* Vc, con
 }  // extern "C"
 
 namespace {
+// gsa_backward's side stream: when the key/value grid is not cut into GQA
+// slices, dQ and then dX run on it beside dK/dV and dW, which stay on the
+// caller's stream.  One per device, created on the device's first backward
+// call with default priority, with the fork and join events; the mutex keeps
+// each call's record/wait pairs together when several host threads use one
+// device.  A stream being captured into a graph gets the sequential order
+// instead (no side stream is created or joined while capturing).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t err = hipSuccess;
+  std::mutex mu;
+};
+std::once_flag g_side_once[kMaxDevices];
+SideStream g_side[kMaxDevices];
+
+SideStream* side_stream(int dev) {
+  std::call_once(g_side_once[dev], [dev] {
+    SideStream& ss = g_side[dev];
+    hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) (void)hipGetLastError();
+    ss.err = e;
+  });
+  return g_side[dev].err == hipSuccess ? &g_side[dev] : nullptr;
+}
+
 // Workspace of gsa_backward, each region 256-byte aligned:
 //   dY  = dY' ⊙ g                 bf16 [B, S, Hq, D]          (gated modes)
 //   per-row statistics            fp32 2 x [B*Hq, Sp]          (base-2 LSE, then D; Sp = S rounded up to 64)
@@ -629,16 +657,43 @@ gsa_status gsa_backward(const void* X, const void* W, const float* G, const void
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   void* dz = gated ? ws + lay.dz : nullptr;
+  // dQ (then dX) on the side stream beside dK/dV (then dW) when the key/value
+  // grid is not sliced: the sliced grid and the dW token chunks share the
+  // partial-sum region, and the sliced (GQA) shapes ran slower that way
+  SideStream* side = nullptr;
+  if (gsa::bwd_kv_slices((int)B, (int)S, (int)Hq, (int)Hkv, (int)D) == 1) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      cap = hipStreamCaptureStatusActive;   // unknown: stay on one stream
+    }
+    int dev = -1;
+    if (cap == hipStreamCaptureStatusNone && hipGetDevice(&dev) == hipSuccess) side = side_stream(dev);
+  }
+  std::unique_lock<std::mutex> lock;
+  if (side) lock = std::unique_lock<std::mutex>(side->mu);
+  hipStream_t st2 = side ? side->s : st;
+  const char* what = "gsa_backward attention launch";
   hipError_t e = gsa::launch_attn_bwd(Q, K, V, dY, Y, G, LSE, dQ, dK, dV, gated ? ws + lay.dy : nullptr,
                                       (float*)(ws + lay.stat), dz, (float*)(ws + lay.part), (int)B, (int)S,
-                                      (int)Hq, (int)Hkv, (int)D, mode, st);
-  if (e != hipSuccess) return hip_result(e, "gsa_backward attention launch");
-  if (gated) {
-    e = gsa::launch_bwd_gemm_dx(dz, W, dX, M, d_model, N, st);
-    if (e != hipSuccess) return hip_result(e, "gsa_backward dX launch");
-    e = gsa::launch_bwd_gemm_dw(X, dz, dW, (float*)(ws + lay.part), M, d_model, N, lay.splits, st);
-    if (e != hipSuccess) return hip_result(e, "gsa_backward dW launch");
+                                      (int)Hq, (int)Hkv, (int)D, mode, st, st2, side ? side->fork : nullptr);
+  if (e == hipSuccess && gated) {
+    what = "gsa_backward dX launch";
+    e = gsa::launch_bwd_gemm_dx(dz, W, dX, M, d_model, N, st2);
+    if (e == hipSuccess) {
+      what = "gsa_backward dW launch";
+      e = gsa::launch_bwd_gemm_dw(X, dz, dW, (float*)(ws + lay.part), M, d_model, N, lay.splits, st);
+    }
   }
+  if (side) {   // the caller's stream waits for whatever the side stream got (also after an error)
+    hipError_t ej = hipEventRecord(side->join, st2);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(st, side->join, 0);
+    if (e == hipSuccess && ej != hipSuccess) {
+      e = ej;
+      what = "gsa_backward join";
+    }
+  }
+  if (e != hipSuccess) return hip_result(e, what);
   return ok();
 }
 

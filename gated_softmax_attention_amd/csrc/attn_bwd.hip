@@ -833,7 +833,7 @@ template <int D>
 static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* dYg,
                                const void* Yg, const float* G, const float* Lse, void* dQ, void* dK,
                                void* dV, void* dY, float* Stat, void* dZ, float* part, int B, int S,
-                               int Hq, int Hkv, int mode, hipStream_t st) {
+                               int Hq, int Hkv, int mode, hipStream_t st, hipStream_t dq_st, hipEvent_t fork) {
   const float scale = 1.0f / sqrtf((float)D);
   const int Sp = bwd_stat_rows(S);
   const int64_t rows = (int64_t)B * S * Hq;
@@ -851,8 +851,14 @@ static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, cons
                        (const bf16*)Yg, G, Lse, (bf16*)dY, Stat, (bf16*)dZ, B, S, Hq, Sp);
     dy_attn = (const bf16*)dYg;   // no gate: the SDPA output's gradient is dY' itself
   }
+  // dQ needs only what the prep pass wrote: on a side stream it runs beside dK/dV
+  if (dq_st != st) {
+    hipError_t e = hipEventRecord(fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(dq_st, fork, 0);
+    if (e != hipSuccess) return e;
+  }
   const int nq = ceil_div(S, bwd::QT);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((int64_t)nq * Hq * B)), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((int64_t)nq * Hq * B)), dim3(256), 0, dq_st,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, dy_attn, (const float*)Stat, (bf16*)dQ,
                      B, S, Hq, Hkv, nq, Sp, scale);
   constexpr bool vlds = D == 128;
@@ -893,12 +899,12 @@ static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, cons
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const void* dYg, const void* Yg,
                            const float* G, const float* Lse, void* dQ, void* dK, void* dV, void* dY,
                            float* Stat, void* dZ, float* part, int B, int S, int Hq, int Hkv, int D,
-                           int mode, hipStream_t stream) {
+                           int mode, hipStream_t stream, hipStream_t dq_stream, hipEvent_t fork) {
   if (D == 128)
     return launch_bwd_d<128>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Stat, dZ, part, B, S, Hq, Hkv, mode,
-                             stream);
+                             stream, dq_stream, fork);
   return launch_bwd_d<64>(Q, K, V, dYg, Yg, G, Lse, dQ, dK, dV, dY, Stat, dZ, part, B, S, Hq, Hkv, mode,
-                          stream);
+                          stream, dq_stream, fork);
 }
 
 }  // namespace gsa

@@ -270,6 +270,13 @@ size_t gsa_backward_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hk
  *        bytes, 16-byte aligned; contents on entry do not matter.
  * Requires dtype GSA_BF16, D in {64, 128}, Hq % Hkv == 0, and with a gate
  * d_model % 8 == 0 and N % 8 == 0.  The results are deterministic (no atomics).
+ * Stream order: the call's work starts after earlier work on `stream`, and
+ * later work on `stream` starts after all of it.  Inside that, when the
+ * key/value grid is not cut into GQA slices, the dQ and dX kernels run on a
+ * library-owned side stream of the current device (created on its first such
+ * call, default priority) beside the dK/dV and dW kernels, forked from and
+ * joined back to `stream` with events; while `stream` is being captured into
+ * a graph every kernel goes on `stream` in sequence instead.
  */
 gsa_status gsa_backward(const void* X, const void* W, const float* G, const void* Q, const void* K,
                         const void* V, const void* Y, const float* LSE, const void* dY, void* dX,

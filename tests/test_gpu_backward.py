@@ -226,3 +226,40 @@ def test_backward_full_size_sampled(name):
         rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
         print(f"  {name} {n}: rel_fro={rel:.3e}", flush=True)
         assert rel <= 1e-2
+
+
+# --------------------------------------------------------------- stream order: side stream and graph capture
+def test_backward_graph_replay_matches_eager():
+    """On an MHA shape (key/value grid not sliced) the eager call runs dQ and dX
+    on the library's side stream; captured into a graph, every kernel runs in
+    sequence on the capturing stream.  Every replay, with eager work and
+    synchronisations between the replays, must give the eager call's bits."""
+    cfg = small_cfg(2, 640, 4, 4, 128, "elementwise", dm=256)
+    inp = make_inputs(cfg, seed=21, device=DEV)
+    dY = make_grad(cfg, seed=21, device=DEV)
+    G = gsa.gate_logits(inp["X"], inp["W"])
+    Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, "elementwise")
+    args = (inp["X"], inp["W"], G, inp["Q"], inp["K"], inp["V"], Y, LSE, dY, "elementwise")
+    eager = gsa.backward(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture, as torch advises
+        gsa.backward(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = gsa.backward(*args)
+    dY2 = -dY
+    for rep in range(3):
+        other = gsa.backward(*args[:8], dY2, "elementwise")   # eager work between replays
+        torch.cuda.synchronize()
+        for n in ("dQ", "dK", "dV", "dX"):
+            captured[n].zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in ("dQ", "dK", "dV", "dX"):
+            assert torch.equal(_bits(captured[n]), _bits(eager[n])), (rep, n)
+        assert torch.equal(captured["dW"].cpu(), eager["dW"].cpu()), rep
+        assert not torch.equal(_bits(other["dQ"]), _bits(eager["dQ"]))
