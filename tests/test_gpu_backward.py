@@ -263,3 +263,25 @@ def test_backward_graph_replay_matches_eager():
             assert torch.equal(_bits(captured[n]), _bits(eager[n])), (rep, n)
         assert torch.equal(captured["dW"].cpu(), eager["dW"].cpu()), rep
         assert not torch.equal(_bits(other["dQ"]), _bits(eager["dQ"]))
+
+
+def test_backward_on_a_user_stream_orders_its_work():
+    """Called on a stream of the caller's, the backward's side-stream kernels are
+    joined back to it: work the caller enqueues next on that stream sees the
+    finished gradients (copies made right after the call, with no
+    synchronisation, equal the gradients of a call on the default stream)."""
+    cfg = small_cfg(2, 1100, 8, 8, 128, "elementwise", dm=512)
+    inp = make_inputs(cfg, seed=33, device=DEV)
+    dY = make_grad(cfg, seed=33, device=DEV)
+    ref = run_backward(inp, dY, "elementwise")
+    G = gsa.gate_logits(inp["X"], inp["W"])
+    Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, "elementwise")
+    torch.cuda.synchronize()
+    user = torch.cuda.Stream()
+    with torch.cuda.stream(user):
+        out = gsa.backward(inp["X"], inp["W"], G, inp["Q"], inp["K"], inp["V"], Y, LSE, dY, "elementwise")
+        copies = {n: out[n].clone() for n in ("dQ", "dK", "dV", "dX", "dW")}
+    torch.cuda.synchronize()
+    for n in ("dQ", "dK", "dV", "dX"):
+        assert torch.equal(_bits(copies[n]), _bits(ref[n])), n
+    assert torch.equal(copies["dW"].cpu(), ref["dW"].cpu())
