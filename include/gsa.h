@@ -16,8 +16,10 @@
  * Conventions for every entry point:
  *  - Pointers X, W, G, Q, K, V, Y, workspace are DEVICE pointers owned by the
  *    caller, to contiguous row-major tensors, each 16-byte aligned.  The library
- *    allocates nothing and keeps no per-call state (gsa_decode_noalloc keeps its
- *    split partials in a fixed device array inside the library).
+ *    allocates no device memory and keeps no per-call state (gsa_decode_noalloc
+ *    keeps its split partials in a fixed device array inside the library;
+ *    gsa_backward creates one side stream and two events per device on its
+ *    first call there, kept until the process ends).
  *  - dtype (gsa_dtype) is the element type of X, W, Q, K, V and Y'.  G is always
  *    float32.  Arithmetic is float32 (bf16 inputs multiply exactly into float32
  *    accumulators on the matrix cores).
