@@ -140,3 +140,33 @@ def test_gated_decode_one_call(B, L, Hq, Hkv, D, mode, dtype, dm):
     itype = torch.int16 if dtype == "bf16" else torch.int32
     assert torch.equal(Y.view(itype), Y2.view(itype))
     report(f64(Y), oracle_decode_by_batch(inp, mode), TOL[dtype], f"gated decode {mode} {dtype} B{B} L{L}")
+
+
+def test_decode_at_the_per_batch_size_limit():
+    """The largest cache a batch may hold: the kernels address one batch's K and
+    V with 32-bit byte offsets, so L·Hkv·D·4 must stay below 2 GiB.  Here
+    L = 2^22 − 8 keys of one 128-dim key/value head (just under the limit), two
+    batches, so the second batch's cache starts past 2 GiB into K and V; every
+    output against the oracle.  One more key per batch (L = 2^22) is refused."""
+    L = (1 << 22) - 8
+    cfg = dec_cfg(2, L, 4, 1, 128, "headwise", "bf16", dm=256)
+    print(f"  decode B2 L{L} 4/1x128 headwise: generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=17, device=DEV)
+    # one key per batch that query head 0 attends to almost entirely (key L-3 of
+    # batch 1 lies within 2 KB of the end of the cache), so head 0's output is
+    # close to that key's value row and a wrong offset shows as an O(1) error
+    for b, kb in ((0, (1 << 21) + 5), (1, L - 3)):
+        inp["K"][b, kb, 0] = (inp["Q"][b, 0, 0].float() * 4).to(torch.bfloat16)
+    Y, _ = run(inp, "headwise")
+    assert not torch.isnan(Y.float()).any()
+    print("  oracle, one batch at a time", flush=True)
+    want = oracle_decode_by_batch(inp, "headwise")
+    report(f64(Y), want, TOL["bf16"], f"decode L={L}, 2 batches")
+    assert float(np.abs(want[:, 0, 0]).max()) > 0.5   # head 0 really follows its planted key
+    del inp, Y
+    torch.cuda.empty_cache()
+    big = torch.empty((1, 1 << 22, 1, 128), dtype=torch.bfloat16, device=DEV)
+    Q = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gsa.GsaError) as err:
+        gsa.decode(Q, big, big, None, "none")
+    assert "exceeds" in str(err.value)
