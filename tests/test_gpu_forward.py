@@ -201,6 +201,44 @@ def test_long_sequence_near_the_size_limit_sampled():
     assert not torch.isnan(Y.float()).any()
 
 
+def test_forward_at_the_per_batch_size_limit():
+    """The largest Q a batch may hold: the kernels address one batch's Q (and
+    Y) with 32-bit byte offsets, so S·Hq·D·4 must stay below 2 GiB.  Two batches
+    of S = 65528 rows of 64 query heads (8 key/value heads, D 128, headwise
+    gate): S·Hq·D·4 is 2^31 − 262144, and the second batch starts 1 GiB into Q
+    and Y.  For rows and heads at the largest offsets a key a few positions back
+    is made to dominate the row (its key is 4 × the query), so a wrong offset
+    shows as an O(1) error; sampled rows of every head against the oracle.
+    S = 65536 rows of 64 heads is refused."""
+    S = 65528
+    cfg = CONFIGS["gqa_prefill"].with_(name="lim", B=2, S=S, d_model=256, Hq=64, Hkv=8, mode="headwise")
+    print(f"  forward B2 S{S} 64/8x128 headwise: generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=23, device=DEV)
+    G = cfg.Hq // cfg.Hkv
+    planted = [(S - 1, cfg.Hq - 1), (S - 1, 0), (S // 2, cfg.Hq - 1), (64, 5)]
+    for b in range(cfg.B):
+        for i, h in planted:
+            inp["K"][b, i - 3, h // G] = (inp["Q"][b, i, h].float() * 4).to(torch.bfloat16)
+    Y, _ = run(inp, cfg.mode, guard=False)
+    assert not torch.isnan(Y.float()).any()
+    rows = sorted({0, 1, 64, 127, 128, S // 2, S - 129, S - 2, S - 1})
+    idx = torch.tensor(rows, device=DEV)
+    print("  oracle on sampled rows", flush=True)
+    want = oracle_rows(f64(inp["X"][:, idx]), f64(inp["W"]), f64(inp["Q"][:, idx]),
+                       f64(inp["K"]), f64(inp["V"]), cfg.mode, rows)
+    report(f64(Y[:, idx]), want, TOL["bf16"], f"S={S}, 64 heads, sampled rows")
+    for b in range(cfg.B):   # the planted rows really follow their key
+        for i, h in planted:
+            assert float(np.abs(want[b, rows.index(i), h]).max()) > 0.5, (b, i, h)
+    del inp, Y
+    torch.cuda.empty_cache()
+    Qbig = torch.empty((1, 65536, 64, 128), dtype=torch.bfloat16, device=DEV)
+    Kbig = torch.empty((1, 65536, 8, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gsa.GsaError) as err:
+        gsa.forward(Qbig, Kbig, Kbig, None, "none")
+    assert "exceeds" in str(err.value)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_extreme_scores(dtype):
     """Q and K scaled by 8: scores reach several hundred, rows are nearly one-hot
