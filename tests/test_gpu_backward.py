@@ -285,3 +285,48 @@ def test_backward_on_a_user_stream_orders_its_work():
     for n in ("dQ", "dK", "dV", "dX"):
         assert torch.equal(_bits(copies[n]), _bits(ref[n])), n
     assert torch.equal(copies["dW"].cpu(), ref["dW"].cpu())
+
+
+def test_backward_from_two_host_threads():
+    """Two host threads, each with its own stream and inputs, call the backward
+    at the same time (the library's side stream and events are shared per
+    device, guarded by a lock): each thread's gradients equal those of a call
+    made alone, bit for bit."""
+    import threading
+    cfgs = [small_cfg(2, 700, 8, 8, 128, "elementwise", dm=256), small_cfg(1, 900, 8, 8, 128, "headwise", dm=256)]
+    cases = []
+    for i, cfg in enumerate(cfgs):
+        inp = make_inputs(cfg, seed=50 + i, device=DEV)
+        dY = make_grad(cfg, seed=50 + i, device=DEV)
+        ref = run_backward(inp, dY, cfg.mode)
+        G = gsa.gate_logits(inp["X"], inp["W"])
+        Y, LSE = gsa.forward_lse(inp["Q"], inp["K"], inp["V"], G, cfg.mode)
+        cases.append((cfg, inp, dY, G, Y, LSE, ref))
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+
+    def worker(i):
+        try:
+            cfg, inp, dY, G, Y, LSE, _ = cases[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for _ in range(5):
+                    out = gsa.backward(inp["X"], inp["W"], G, inp["Q"], inp["K"], inp["V"], Y, LSE, dY, cfg.mode)
+                    outs.append({n: out[n].clone() for n in ("dQ", "dK", "dV", "dX", "dW")})
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:   # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, (_, _, _, _, _, _, ref) in enumerate(cases):
+        for out in results[i]:
+            for n in ("dQ", "dK", "dV", "dX"):
+                assert torch.equal(_bits(out[n]), _bits(ref[n])), (i, n)
+            assert torch.equal(out["dW"].cpu(), ref["dW"].cpu()), i
