@@ -475,7 +475,12 @@ def _mapped(path, mode="r"):
     return _MAPS[key]
 
 
-def _pool_init():
+_READY = None
+
+
+def _pool_init(barrier=None):
+    global _READY
+    _READY = barrier
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)      # one BLAS thread per worker: the pool supplies the parallelism
@@ -484,6 +489,9 @@ def _pool_init():
 
 
 def _pool_ready(_):
+    """Imports the oracle, then waits for every worker at the barrier: a worker
+    held there takes no second task, so each worker runs one of these and all
+    have started before the timing begins."""
     import numpy  # noqa: F401
     import oracle  # noqa: F401
     try:
@@ -491,6 +499,8 @@ def _pool_ready(_):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = -1
+    if _READY is not None:
+        _READY.wait(timeout=300)
     return os.getpid(), threads
 
 
@@ -586,8 +596,10 @@ def cpu_baseline(args, runs, pool_size):
     saved = {k: os.environ.get(k) for k in thread_vars}
     os.environ.update({k: "1" for k in thread_vars})
     try:
-        pool = ctx.Pool(pool_size, initializer=_pool_init)
-        ready = pool.map(_pool_ready, range(pool_size))   # interpreter start-up, outside the timing
+        barrier = ctx.Barrier(pool_size)
+        pool = ctx.Pool(pool_size, initializer=_pool_init, initargs=(barrier,))
+        # interpreter start-up and imports, outside the timing: one task per worker
+        ready = pool.map(_pool_ready, range(pool_size), chunksize=1)
         print(f"# oracle pool: {len({p for p, _ in ready})} workers, BLAS threads per worker "
               f"{sorted({t for _, t in ready})}", file=sys.stderr, flush=True)
     finally:
